@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Verify-attention benchmark on one MI355X: verify-step latency and effective
+KV bandwidth (fraction of the HBM roofline) against context length.
+
+A step is one verify call: the ancestor mask, the split-KV partial attention
+and the log-sum-exp merge, over one batch of synthetic input. Inputs are in
+HBM before the timed region starts. To measure HBM rather than the 256 MB
+Infinity Cache, the steps cycle over R replicas of the workload whose KV rows
+sit in disjoint regions of one pool (R x KV bytes >= 1 GiB); every replica
+holds the same logical rows, so every step computes the same result. The R
+calls are captured in one hipGraph and replayed.
+
+Prints one JSON line. Options: --workload (C1, C2, C3, C4a, C4b, C5),
+--nsplit, --steps, --warmup, --no-sweep, --no-cpu.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify-step latency (µs) + effective KV GB/s (% HBM roofline) vs context length"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+QK_DIM, V_DIM = 576, 512
+KV_ROW_BYTES = QK_DIM * 2  # one bf16 latent row per key
+ROTATE_BYTES = 1 << 30     # >= 4 x the 256 MB Infinity Cache
+
+WORKLOAD_TEXT = {
+    "C1": "1 request, context 256, 4-node chain, 8 heads, page size 1",
+    "C2": "1 request, context 4,096, 16-node random tree, 8 heads, page size 1 scattered in a 200k-slot pool",
+    "C3": "1 request, context 65,536, 32-node tree (depth <= 8), 8 heads, page size 1 scattered",
+    "C4a": "1 request, context 184,728, 32-node tree, 8 heads, page size 1, fragmented page table",
+    "C4b": "1 request, context 184,728, 32-node tree, 8 heads, page size 1, contiguous slots",
+    "C5": "8 requests, contexts log-uniform in [1k, 128k], 12-node chain, 8 heads, page size 64",
+}
+
+
+# ---------------------------------------------------------------- accounting
+
+def kv_bytes(seq_lens) -> int:
+    """Latent bytes a verify call must read: one 1,152-byte row per key."""
+    return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * KV_ROW_BYTES
+
+
+def partial_algorithmic_bytes(seq_lens, nodes, heads, page_size) -> int:
+    """Bytes the split-partial kernel must move by the method's definition: KV
+    rows, page-table entries, queries, tree parents and sequence lengths.
+    Split partials are implementation traffic and are not counted."""
+    keys = int(np.sum(np.asarray(seq_lens, dtype=np.int64)))
+    b = len(seq_lens)
+    pages = int(sum(math.ceil(int(n) / page_size) for n in seq_lens))
+    return keys * KV_ROW_BYTES + pages * 4 + b * nodes * heads * KV_ROW_BYTES + b * nodes * 4 + b * 4
+
+
+def step_algorithmic_bytes(seq_lens, nodes, heads, page_size) -> int:
+    b = len(seq_lens)
+    return partial_algorithmic_bytes(seq_lens, nodes, heads, page_size) + b * nodes * heads * (V_DIM * 2 + 4)
+
+
+def algorithmic_flops(seq_lens, nodes, heads) -> int:
+    """QK^T (2 x 576) and PV (2 x 512) multiply-adds per (row, key)."""
+    keys = int(np.sum(np.asarray(seq_lens, dtype=np.int64)))
+    return keys * nodes * heads * 2 * (QK_DIM + V_DIM)
+
+
+def roof_bound(nodes, heads) -> str:
+    intensity = nodes * heads * 2 * (QK_DIM + V_DIM) / KV_ROW_BYTES  # flop per KV byte
+    return "mfma" if intensity > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+
+
+def default_nsplit(batch, nodes, heads, max_keys) -> int:
+    """Enough splits to give every CU a workgroup without chunks below 256 keys."""
+    rows = nodes * heads
+    waves = -(-rows // 32)
+    row_blocks = -(-waves // 4)
+    want_wgs = 256
+    per_req = max(1, want_wgs // max(1, batch * row_blocks))
+    return int(max(1, min(per_req, max_keys // 256 if max_keys >= 256 else 1)))
+
+
+# ---------------------------------------------------------------- inputs on the GPU
+
+class Replicated:
+    """R replicas of one logical workload in disjoint pool regions."""
+
+    def __init__(self, torch, logical_rows, q_bits, seq_lens, tree_parent, page_size, replicas, seed):
+        self.torch = torch
+        dev = "cuda"
+        b = len(seq_lens)
+        ps = page_size
+        pages = [math.ceil(int(n) / ps) for n in seq_lens]
+        ptot = sum(pages)
+        self.max_pages = max(pages)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        # logical rows of every request, each padded to whole pages
+        padded = torch.zeros((ptot * ps, QK_DIM), dtype=torch.bfloat16, device=dev)
+        off_rows, off = 0, 0
+        for i in range(b):
+            n = int(seq_lens[i])
+            padded[off_rows:off_rows + n] = logical_rows[off:off + n]
+            off_rows += pages[i] * ps
+            off += n
+        self.pool = torch.empty((replicas * ptot * ps, QK_DIM), dtype=torch.bfloat16, device=dev)
+        pool_pages = self.pool.view(replicas * ptot, ps, QK_DIM)
+        self.page_tables = []
+        for r in range(replicas):
+            perm = torch.randperm(ptot, generator=gen, device=dev) + r * ptot
+            pool_pages[perm] = padded.view(ptot, ps, QK_DIM)
+            pt = torch.full((b, self.max_pages), -1, dtype=torch.int32, device=dev)
+            o = 0
+            for i in range(b):
+                pt[i, :pages[i]] = perm[o:o + pages[i]].to(torch.int32)
+                o += pages[i]
+            self.page_tables.append(pt)
+        del padded
+        self.q = q_bits
+        self.seq_lens = torch.tensor(np.asarray(seq_lens, dtype=np.int32), device=dev)
+        self.tree_parent = torch.tensor(np.asarray(tree_parent, dtype=np.int32), device=dev)
+        self.page_size = ps
+        self.replicas = replicas
+
+
+def bf16_from_bits(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def logical_rows_of_case(case):
+    rows = []
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        p = np.arange(n)
+        slots = case.page_table[b][p // case.page_size].astype(np.int64) * case.page_size + p % case.page_size
+        rows.append(case.kv[slots])
+    return np.concatenate(rows)
+
+
+# ---------------------------------------------------------------- timing
+
+def capture(torch, fns):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def run_steps(torch, g_full, per_graph, g_rem, rem, steps):
+    n_full = steps // per_graph
+    for _ in range(n_full):
+        g_full.replay()
+    if rem:
+        g_rem.replay()
+
+
+def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, steps, warmup):
+    """Returns (ms per step over exactly `steps` steps, partial-kernel us per
+    launch, out, lse, workspace)."""
+    b = rep.q.shape[0]
+    out = torch.empty((b, nodes, heads, V_DIM), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, nodes, heads), dtype=torch.float32, device="cuda")
+    desc = mv.desc_for(rep.q, rep.pool, rep.page_tables[0], page_size=rep.page_size, nsplit=nsplit,
+                       sm_scale=sm_scale)
+    ws = mv.alloc_workspace(desc)
+
+    def full_call(r):
+        return lambda: mv.verify_attention(rep.q, rep.pool, rep.page_tables[r], rep.seq_lens, rep.tree_parent,
+                                           out, lse, ws, page_size=rep.page_size, nsplit=nsplit,
+                                           sm_scale=sm_scale)
+
+    def partial_call(r):
+        return lambda: mv.verify_partial(desc, rep.q, rep.pool, rep.page_tables[r], rep.seq_lens, rep.tree_parent,
+                                         ws)
+
+    R = rep.replicas
+    per_graph = min(R, steps)
+    g_full = capture(torch, [full_call(r) for r in range(per_graph)])
+    rem = steps % per_graph
+    g_rem = capture(torch, [full_call(r) for r in range(rem)]) if rem else None
+    # warmup: W untimed steps
+    w_graph = min(R, max(warmup, 1))
+    g_w = capture(torch, [full_call(r) for r in range(w_graph)])
+    for _ in range(max(1, warmup // w_graph)):
+        g_w.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    run_steps(torch, g_full, per_graph, g_rem, rem, steps)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / steps
+
+    # the dominant kernel alone, timed with events on the stream it runs on
+    g_p = capture(torch, [partial_call(r) for r in range(R)])
+    g_p.replay()
+    torch.cuda.synchronize()
+    reps = max(1, min(50, (steps + R - 1) // R))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g_p.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    partial_us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+    # leave the full result of replica 0 in out/lse
+    full_call(0)()
+    torch.cuda.synchronize()
+    return ms_per_step, partial_us, out, lse, ws
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(case, budget_s=10.0, max_reps=20):
+    """Time the oracle (as it stands) on this host's cores on the same workload."""
+    from oracle import oracle_case  # the checker's leg of the benchmark only
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    times, ref = [], None
+    t_start = time.perf_counter()
+    while len(times) < max_reps:
+        t = time.perf_counter()
+        ref = oracle_case(case)
+        times.append(time.perf_counter() - t)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    med = statistics.median(times)
+    return med, len(times), threads, ref
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------- main
+
+def measure_case(torch, mv, case, nsplit, steps, warmup, seed):
+    rows = logical_rows_of_case(case)
+    lr = bf16_from_bits(torch, rows).cuda()
+    q = bf16_from_bits(torch, case.q).cuda()
+    kvb = kv_bytes(case.seq_lens)
+    replicas = max(1, math.ceil(ROTATE_BYTES / max(kvb, 1)))
+    rep = Replicated(torch, lr, q, case.seq_lens, case.tree_parent, case.page_size, replicas, seed)
+    del lr
+    res = time_workload(torch, mv, rep, case.num_nodes, case.num_heads, nsplit, case.sm_scale, steps, warmup)
+    return res, rep
+
+
+def sweep_point(torch, mv, context, nodes, heads=8, seed=7):
+    """A context-sweep point generated on the GPU (seeded): N(0,1) bf16 rows,
+    uniform-parent tree (depth <= 8 for 32 nodes), page size 1."""
+    from workloads.gen import tree_depth_capped, tree_uniform
+
+    rng = np.random.default_rng(seed + context + nodes)
+    tree = tree_depth_capped(nodes, 8, rng) if nodes == 32 else tree_uniform(nodes, rng)
+    n = context + nodes
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed * 1000 + nodes)
+    rows = torch.randn((n, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((1, nodes, heads, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    kvb = kv_bytes([n])
+    replicas = max(1, math.ceil(ROTATE_BYTES / kvb))
+    rep = Replicated(torch, rows, q, [n], tree[None, :], 1, replicas, seed)
+    del rows
+    nsplit = default_nsplit(1, nodes, heads, n)
+    steps = replicas * max(2, 64 // replicas)
+    ms, partial_us, *_ = time_workload(torch, mv, rep, nodes, heads, nsplit, 1.0 / math.sqrt(192.0), steps,
+                                       replicas)
+    lat_us = ms * 1e3
+    eff = kvb / (lat_us * 1e-6) / 1e9
+    pbytes = partial_algorithmic_bytes([n], nodes, heads, 1)
+    flops = algorithmic_flops([n], nodes, heads)
+    entry = dict(workload=f"context {context}, {nodes}-node tree, {heads} heads, page size 1",
+                 context=context, nodes=nodes, rows=nodes * heads, nsplit=nsplit, replicas=replicas,
+                 latency_us=round(lat_us, 2), eff_kv_gbs=round(eff, 1), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
+                 partial_us=round(partial_us, 2),
+                 partial_hbm_frac=round(pbytes / (partial_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 partial_mfma_frac=round(flops / (partial_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 bound=roof_bound(nodes, heads))
+    del rep
+    torch.cuda.empty_cache()
+    return entry
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=256)
+    ap.add_argument("--workload", default="C2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--nsplit", type=int, default=None)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--seed", type=int, default=1234)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the verify kernel works on one GPU's "
+                                   "share (8 heads of a tensor-parallel rank) and no multi-GPU path is built",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_decoding_mla_amd as mv
+    from workloads import make_case
+
+    mv.load_library()
+    case = make_case(args.workload, nsplit=args.nsplit)
+    nsplit = case.nsplit
+    (ms, partial_us, out, lse, ws), rep = measure_case(torch, mv, case, nsplit, args.steps, args.warmup,
+                                                        args.seed)
+    dev_err = mv.device_error(ws)
+    lat_us = ms * 1e3
+    kvb = kv_bytes(case.seq_lens)
+    eff = kvb / (lat_us * 1e-6) / 1e9
+    bound = roof_bound(case.num_nodes, case.num_heads)
+    pbytes = partial_algorithmic_bytes(case.seq_lens, case.num_nodes, case.num_heads, case.page_size)
+    pflops = algorithmic_flops(case.seq_lens, case.num_nodes, case.num_heads)
+    if bound == "hbm":
+        achieved = pbytes / (partial_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+    else:
+        achieved = pflops / (partial_us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None)
+    roof.update(kernel="verify_partial_kernel", kernel_us=round(partial_us, 3), bytes_per_launch=pbytes,
+                flops_per_launch=pflops)
+    gpu_out = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    gpu_lse = lse.cpu().numpy()
+    del rep, out, lse, ws
+    torch.cuda.empty_cache()
+
+    line = dict(metric=METRIC, value=round(eff, 2), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=round(ms, 6), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+                data="synthetic",
+                config=dict(workload=f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                            context=case.meta["context"], nodes=case.num_nodes, heads=case.num_heads,
+                            page_size=case.page_size, nsplit=nsplit, rows=case.num_nodes * case.num_heads,
+                            replicas=math.ceil(ROTATE_BYTES / kvb), parallelism="none (1 GPU)"),
+                latency_us=round(lat_us, 3), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
+                roofline=roof, device_error=dev_err)
+
+    if not args.no_cpu:
+        med, reps, threads, ref = cpu_baseline(case)
+        line["cpu_baseline"] = dict(value=round(kvb / med / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
+                                    sample=f"whole {args.workload} verify call, {reps} timed runs, median "
+                                           f"{med * 1e6:.0f} us; CPU {cpu_model()}")
+        from oracle import bf16_bits_to_f64
+        o = bf16_bits_to_f64(gpu_out)
+        line["parity_vs_oracle"] = dict(out_max_abs=float(np.abs(o - ref[0]).max()),
+                                        lse_max_abs=float(np.abs(gpu_lse - ref[1]).max()))
+
+    if not args.no_sweep:
+        sweep = []
+        for ctx, t in [(65_536, 9), (65_536, 16), (131_072, 9), (184_728, 9), (184_728, 16), (65_536, 32)]:
+            sweep.append(sweep_point(torch, mv, ctx, t))
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,50 @@
+// Internal launch interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mlav {
+
+constexpr int kQkDim = 576;       // 512 latent + 64 rope
+constexpr int kVDim = 512;        // V = leading 512 entries of the latent row
+constexpr int kMaxNodes = 64;     // ancestor sets are 64-bit masks
+constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block of (node, head) rows per wave
+constexpr int kHeaderBytes = 256; // workspace header; word 0 is the device error word
+
+// Everything one verify call needs, resolved on the host from the descriptor.
+struct VerifyLaunch {
+  const uint16_t* q;           // bf16 [B, T, H, 576]
+  const uint8_t* kv;           // bf16 rows, byte pointer
+  const int32_t* page_table;   // [B, max_pages]
+  const int32_t* seq_lens;     // [B]
+  const int32_t* tree_parent;  // [B, T]
+  uint16_t* out;               // bf16 [B, T, H, 512]
+  float* lse;                  // [B, T, H]
+  uint32_t* err;               // device error word (workspace head)
+  float* part_lse;             // [B, nsplit, rows_pad] log2-domain partial lse
+  float* part_o;               // fragment-ordered partial outputs (fp32)
+  int64_t kv_row_bytes;        // bytes between kv rows
+  int64_t num_slots;
+  int32_t batch, nodes, heads, rows, rows_pad, waves_per_wg, row_blocks;
+  int32_t nsplit, page_shift, max_pages;
+  int32_t capacity;            // max_pages * page_size (clamp bound for seq_lens)
+  float scale_log2;            // sm_scale * log2(e)
+};
+
+// Rows (node, head) are grouped in waves of 32; a workgroup holds 1..4 waves.
+struct RowPlan {
+  int rows, waves_per_wg, row_blocks, rows_pad;
+};
+RowPlan plan_rows(int nodes, int heads);
+
+size_t workspace_bytes(int batch, int nsplit, int rows_pad);
+size_t part_lse_offset();
+size_t part_o_offset(int batch, int nsplit, int rows_pad);
+
+hipError_t launch_tree_mask(const int32_t* tree_parent, uint64_t* anc, int batch, int nodes,
+                            uint32_t* err, hipStream_t stream);
+hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream);
+hipError_t launch_combine(const VerifyLaunch& L, hipStream_t stream);
+
+}  // namespace mlav

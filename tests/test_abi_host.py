@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/mla_verify.h declares, sizes workspaces by its formula
+and rejects bad descriptors and pointers before enqueuing anything (these
+calls return before any HIP runtime call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_mla_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == {"mla_verify_workspace_bytes", "mla_build_tree_mask", "mla_verify_attention",
+                          "mla_verify_partial", "mla_verify_combine", "mla_status_string",
+                          "mla_verify_abi_version"}
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    lib = bd.load_library()
+    assert lib.mla_verify_abi_version() == 1
+    for code in range(-6, 1):
+        assert lib.mla_status_string(code)
+    assert lib.mla_status_string(-4) == b"workspace too small"
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_nodes=16, num_heads=8, page_size=1, max_pages=5000, nsplit=64, num_kv_slots=200000)
+    base.update(kw)
+    return bd.make_desc(**base)
+
+
+def test_workspace_formula():
+    # 16 nodes x 8 heads = 128 rows = 4 waves of 32 in one row block.
+    d = _desc()
+    rows_pad, b, s = 128, 2, 64
+    lse_bytes = b * s * rows_pad * 4
+    o_off = (256 + lse_bytes + 255) // 256 * 256
+    assert bd.workspace_bytes(d) == o_off + b * s * rows_pad * 512 * 4
+    # 9 nodes x 8 heads = 72 rows -> 3 waves (96 padded rows)
+    d = _desc(num_nodes=9, batch=1, nsplit=3)
+    lse_bytes = 1 * 3 * 96 * 4
+    assert bd.workspace_bytes(d) == (256 + lse_bytes + 255) // 256 * 256 + 3 * 96 * 512 * 4
+    # 32 nodes x 8 heads = 256 rows -> two row blocks of 128
+    d = _desc(num_nodes=32, batch=1, nsplit=1)
+    assert bd.workspace_bytes(d) == (256 + 256 * 4 + 255) // 256 * 256 + 256 * 512 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_nodes=0), -2), (dict(num_nodes=65), -2), (dict(batch=0), -2), (dict(num_heads=0), -2),
+    (dict(nsplit=0), -2), (dict(max_pages=0), -2), (dict(num_kv_slots=0), -2),
+    (dict(page_size=3), -3), (dict(page_size=0), -3), (dict(head_dim_qk=512), -3), (dict(head_dim_v=576), -3),
+    (dict(kv_row_stride=570), -2), (dict(kv_row_stride=580), -2), (dict(max_pages=3, num_nodes=4), -2),
+])
+def test_bad_descriptor_rejected(kw, status):
+    d = _desc(**kw)
+    assert bd.workspace_bytes(d) == 0
+    lib = bd.load_library()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st = lib.mla_verify_attention(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert st == status
+
+
+def test_null_misaligned_and_small_workspace():
+    lib = bd.load_library()
+    d = _desc()
+    need = bd.workspace_bytes(d)
+    a = 1 << 20
+    args = [a] * 8
+    assert lib.mla_verify_attention(None, *args, need, None) == -1
+    for i in range(8):
+        bad = list(args)
+        bad[i] = None
+        assert lib.mla_verify_attention(ctypes.byref(d), *bad, need, None) == -1
+    for i in (0, 1, 5, 7):  # q, kv_cache, out, workspace need 16-byte alignment
+        bad = list(args)
+        bad[i] = a + 8
+        assert lib.mla_verify_attention(ctypes.byref(d), *bad, need, None) == -5
+    for i in (2, 3, 4, 6):  # int32 / fp32 arrays need 4-byte alignment
+        bad = list(args)
+        bad[i] = a + 2
+        assert lib.mla_verify_attention(ctypes.byref(d), *bad, need, None) == -5
+    assert lib.mla_verify_attention(ctypes.byref(d), *args, need - 1, None) == -4
+
+
+def test_stage_entry_points_check_arguments():
+    lib = bd.load_library()
+    d = _desc()
+    need = bd.workspace_bytes(d)
+    a = 1 << 20
+    assert lib.mla_verify_partial(ctypes.byref(d), None, a, a, a, a, a, need, None) == -1
+    assert lib.mla_verify_partial(ctypes.byref(d), a, a, a, a, a, None, need, None) == -1
+    assert lib.mla_verify_partial(ctypes.byref(d), a + 8, a, a, a, a, a, need, None) == -5
+    assert lib.mla_verify_partial(ctypes.byref(d), a, a, a, a, a, a, need - 1, None) == -4
+    assert lib.mla_verify_combine(ctypes.byref(d), None, a, a, need, None) == -1
+    assert lib.mla_verify_combine(ctypes.byref(d), a + 8, a, a, need, None) == -5
+    assert lib.mla_verify_combine(ctypes.byref(d), a, a, a, need - 1, None) == -4
+    bad = _desc(nsplit=0)
+    assert lib.mla_verify_combine(ctypes.byref(bad), a, a, a, need, None) == -2
+
+
+def test_tree_mask_argument_checks():
+    lib = bd.load_library()
+    a = 1 << 20
+    assert lib.mla_build_tree_mask(None, a, 1, 4, None, None) == -1
+    assert lib.mla_build_tree_mask(a, None, 1, 4, None, None) == -1
+    assert lib.mla_build_tree_mask(a, a, 0, 4, None, None) == -2
+    assert lib.mla_build_tree_mask(a, a, 1, 0, None, None) == -2
+    assert lib.mla_build_tree_mask(a, a, 1, 65, None, None) == -2
