@@ -47,6 +47,10 @@ WORKLOAD_TEXT = {
 }
 
 
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 # ---------------------------------------------------------------- accounting
 
 def kv_bytes(seq_lens) -> int:
@@ -337,7 +341,9 @@ def main():
     from workloads import make_case
 
     mv.load_library()
+    log(f"generating {args.workload}")
     case = make_case(args.workload, nsplit=args.nsplit)
+    log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warmup")
     nsplit = case.nsplit
     (ms, partial_us, out, lse, ws), rep = measure_case(torch, mv, case, nsplit, args.steps, args.warmup,
                                                         args.seed)
@@ -373,7 +379,9 @@ def main():
                 latency_us=round(lat_us, 3), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
                 roofline=roof, device_error=dev_err)
 
+    log(f"{args.workload}: {lat_us:.2f} us/step, partial kernel {partial_us:.2f} us")
     if not args.no_cpu:
+        log("timing the CPU oracle")
         med, reps, threads, ref = cpu_baseline(case)
         line["cpu_baseline"] = dict(value=round(kvb / med / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
                                     sample=f"whole {args.workload} verify call, {reps} timed runs, median "
@@ -387,6 +395,7 @@ def main():
         sweep = []
         for ctx, t in [(65_536, 9), (65_536, 16), (131_072, 9), (184_728, 9), (184_728, 16), (65_536, 32)]:
             sweep.append(sweep_point(torch, mv, ctx, t))
+            log(f"sweep context {ctx} nodes {t}: {sweep[-1]['latency_us']} us, {sweep[-1]['eff_kv_gbs']} GB/s")
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)
 

@@ -15,6 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_DIR = os.path.join(PKG_DIR, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmla_verify.so")
+PEAKS_PATH = os.path.join(LIB_DIR, "mla_peaks")  # measured roofline denominators
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = ["mla_verify_kernels.hip", "mla_verify_api.cpp"]
 ARCH = "gfx950"
@@ -41,12 +42,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library. Always
-    recompiles. Returns the library path."""
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,7 +53,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950: the shared library and the peak
+    microbenchmark executable. Always recompiles. Returns the library path."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES], verbose)
     os.replace(tmp, LIB_PATH)
+    tmp = PEAKS_PATH + ".tmp"
+    _run([hipcc(), *[f for f in HIP_FLAGS if f != "-fvisibility=hidden"], "-o", tmp,
+          os.path.join(CSRC, "mla_peaks.hip")], verbose)
+    os.replace(tmp, PEAKS_PATH)
     return LIB_PATH
 
 

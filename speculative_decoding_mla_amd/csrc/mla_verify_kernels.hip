@@ -422,21 +422,36 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     }
 }
 
-// Merge of the split partials of 32 rows x 8 columns (one fragment slot) per
-// wave: lse = M + log2 sum_s 2^(lse_s - M), out = sum_s w_s O_s / sum_s w_s,
-// skipping empty splits; the result is rounded to bf16 once.
-__global__ __launch_bounds__(64) void verify_combine_kernel(VerifyLaunch L) {
-  const int lane = threadIdx.x;
+// Merge of the split partials of one fragment slot (32 rows x 8 columns): the
+// four waves of the workgroup take every fourth split, so a slot's partials
+// are read with four waves' worth of loads in flight. Pass 1 finds each row's
+// largest partial lse M; pass 2 accumulates w_s = 2^(lse_s - M) and w_s * O_s
+// (empty splits have lse = -inf and are skipped); the waves' sums are added in
+// LDS. out = sum w_s O_s / sum w_s rounded to bf16 once; lse = M + log2 sum w_s,
+// converted to natural-log units.
+constexpr int kCombineWaves = 4;
+
+__global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(VerifyLaunch L) {
+  __shared__ float red_m[kCombineWaves][32];
+  __shared__ f32x4 red_acc[kCombineWaves][64];
+  __shared__ float red_w[kCombineWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   const int nwb = L.rows_pad / 32;
   const int frag = blockIdx.x & 63;
   const int wb = (blockIdx.x >> 6) % nwb;
   const int b = (blockIdx.x >> 6) / nwb;
-  const int row = wb * 32 + (lane & 31);
-  if (row >= L.rows) return;
+  const int row = wb * 32 + (lane & 31);  // < rows_pad: its partial lse is always written
 
   const float* pl = L.part_lse + static_cast<size_t>(b) * L.nsplit * L.rows_pad + row;
   float mx = -INFINITY;
-  for (int s = 0; s < L.nsplit; ++s) mx = fmaxf(mx, pl[static_cast<size_t>(s) * L.rows_pad]);
+#pragma unroll 8
+  for (int s = w; s < L.nsplit; s += kCombineWaves) mx = fmaxf(mx, pl[static_cast<size_t>(s) * L.rows_pad]);
+  if (lane < 32) red_m[w][lane] = mx;
+  __syncthreads();
+  mx = red_m[0][lane & 31];
+#pragma unroll
+  for (int i = 1; i < kCombineWaves; ++i) mx = fmaxf(mx, red_m[i][lane & 31]);
 
   f32x4 acc = {};
   float wsum = 0.f;
@@ -445,16 +460,24 @@ __global__ __launch_bounds__(64) void verify_combine_kernel(VerifyLaunch L) {
     const f32x4* po = reinterpret_cast<const f32x4*>(L.part_o) +
                       static_cast<size_t>(b) * L.nsplit * split_stride + static_cast<size_t>(wb) * 4096 +
                       frag * 64 + lane;
-#pragma unroll 4
-    for (int s = 0; s < L.nsplit; ++s) {
+#pragma unroll 8
+    for (int s = w; s < L.nsplit; s += kCombineWaves) {
       const float l2 = pl[static_cast<size_t>(s) * L.rows_pad];
-      const bool live = l2 > -INFINITY;
       const f32x4 v = po[s * split_stride];
-      const float w = live ? __builtin_amdgcn_exp2f(l2 - mx) : 0.f;
-      const f32x4 vz = live ? v : f32x4{};
-      acc += w * vz;
-      wsum += w;
+      const bool live = l2 > -INFINITY;
+      const float wt = live ? __builtin_amdgcn_exp2f(l2 - mx) : 0.f;
+      acc += wt * (live ? v : f32x4{});
+      wsum += wt;
     }
+  }
+  red_acc[w][lane] = acc;
+  red_w[w][lane] = wsum;
+  __syncthreads();
+  if (w != 0 || row >= L.rows) return;
+#pragma unroll
+  for (int i = 1; i < kCombineWaves; ++i) {
+    acc += red_acc[i][lane];
+    wsum += red_w[i][lane];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const f32x4 r = acc * inv;
@@ -513,7 +536,7 @@ hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream) {
 
 hipError_t launch_combine(const VerifyLaunch& L, hipStream_t stream) {
   const int cgrid = L.batch * (L.rows_pad / 32) * 64;
-  hipLaunchKernelGGL(verify_combine_kernel, dim3(cgrid), dim3(64), 0, stream, L);
+  hipLaunchKernelGGL(verify_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), 0, stream, L);
   return hipGetLastError();
 }
 

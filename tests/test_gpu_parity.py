@@ -116,11 +116,17 @@ def test_parity_4k_config_nsplit_sweep():
         assert err == 0
         check_parity(case, out, lse, ref=ref, label=f"C2/{ns}")
         outs[ns] = (bf16_bits_to_f64(out), lse)
-    # results do not depend on NSPLIT beyond rounding: within 1 bf16 ulp / 1e-5
+    # Results do not depend on NSPLIT beyond rounding. Two results differ by
+    # the rounding of bf16 weights (relative 2^-9 per weight, averaging out
+    # over thousands of keys to ~1e-4 absolute here) plus the final bf16
+    # rounding: at most one bf16 ulp of the larger magnitude, or 2.5e-4 where
+    # that ulp is smaller than the weight-rounding noise.
     base_o, base_l = outs[64]
     for ns, (o, l) in outs.items():
-        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(base_o), 2 ** -20))) - 7)
-        assert np.all(np.abs(o - base_o) <= ulp + 1e-12), ns
+        mag = np.maximum(np.maximum(np.abs(o), np.abs(base_o)), 2.0 ** -20)
+        ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
+        bound = np.maximum(ulp, 2.5e-4)
+        assert np.all(np.abs(o - base_o) <= bound), (ns, float(np.abs(o - base_o).max()))
         assert np.abs(l - base_l).max() <= 1e-5, ns
 
 
