@@ -282,7 +282,7 @@ def measure_case(torch, mv, case, nsplit, steps, warmup, seed):
     return res, rep
 
 
-def sweep_point(torch, mv, context, nodes, heads=8, seed=7):
+def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None):
     """A context-sweep point generated on the GPU (seeded): N(0,1) bf16 rows,
     uniform-parent tree (depth <= 8 for 32 nodes), page size 1."""
     from workloads.gen import tree_depth_capped, tree_uniform
@@ -298,7 +298,7 @@ def sweep_point(torch, mv, context, nodes, heads=8, seed=7):
     replicas = max(1, math.ceil(ROTATE_BYTES / kvb))
     rep = Replicated(torch, rows, q, [n], tree[None, :], 1, replicas, seed)
     del rows
-    nsplit = default_nsplit(1, nodes, heads, n)
+    nsplit = nsplit or default_nsplit(1, nodes, heads, n)
     steps = replicas * max(2, 64 // replicas)
     ms, partial_us, *_ = time_workload(torch, mv, rep, nodes, heads, nsplit, 1.0 / math.sqrt(192.0), steps,
                                        replicas)
@@ -323,7 +323,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=256)
-    ap.add_argument("--workload", default="C2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="C2",
+                    help="C1, C2, C3, C4a, C4b, C5, or a context-sweep point S<context>_T<nodes>")
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -341,6 +342,15 @@ def main():
     from workloads import make_case
 
     mv.load_library()
+    if args.workload.startswith("S"):
+        ctx, nodes = args.workload[1:].split("_T")
+        e = sweep_point(torch, mv, int(ctx), int(nodes), nsplit=args.nsplit)
+        log(json.dumps(e))
+        print(json.dumps(dict(metric=METRIC, value=e["eff_kv_gbs"], unit="GB/s", n_gpus=1, latency_us=e["latency_us"],
+                              config=dict(workload=e["workload"]), sweep=[e])), flush=True)
+        return
+    if args.workload not in WORKLOAD_TEXT:
+        ap.error(f"unknown workload {args.workload}")
     log(f"generating {args.workload}")
     case = make_case(args.workload, nsplit=args.nsplit)
     log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warmup")

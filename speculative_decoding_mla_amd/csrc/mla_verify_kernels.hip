@@ -13,8 +13,11 @@
 //    row (MLA), so a key tile staged once in LDS feeds every row of the block.
 //  * Key tiles of 32 rows x 1152 B move HBM -> LDS with gfx950's 128-bit
 //    global_load_lds (no VGPR staging), kStages deep, one s_barrier per tile.
-//    Each 16-byte chunk of a row lands at chunk ^ swz(key) inside its 128-byte
-//    group so both LDS read patterns below are free of bank conflicts.
+//    A tile holds the 32 latent parts (1 KiB each, one wave-wide load per key
+//    whose row address is wave-uniform) followed by the 32 rope parts (128 B,
+//    eight keys per load). Each 16-byte chunk lands at chunk ^ swz(key)
+//    inside its 128-byte group so both LDS read patterns below are free of
+//    bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K fragments come from LDS, the wave's 32 query rows stay in VGPRs for the
 //    whole kernel. In the S^T accumulator every lane owns one query row, so the
@@ -62,10 +65,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kKeysPerTile = 32;
-constexpr int kRowBytes = kQkDim * 2;                              // 1152
-constexpr int kChunksPerRow = kRowBytes / 16;                      // 72
+constexpr int kRowBytes = kQkDim * 2;                              // 1152 per key in HBM
+constexpr int kLatentBytes = kVDim * 2;                            // 1024: one wave-wide load
+constexpr int kRopeBytes = kRowBytes - kLatentBytes;               // 128
+constexpr int kRopeBase = kKeysPerTile * kLatentBytes;             // rope part of a tile in LDS
 constexpr int kTileBytes = kKeysPerTile * kRowBytes;               // 36864
-constexpr int kTileInstr = kKeysPerTile * kChunksPerRow / 64;      // 36 wave-wide 1 KiB loads
+constexpr int kRopeInstr = kKeysPerTile * kRopeBytes / 1024;       // 4 loads of 8 keys' rope
+constexpr int kTileInstr = kKeysPerTile + kRopeInstr;              // 36 wave-wide 1 KiB loads
 constexpr int kStages = 4;
 constexpr int kSlotCap = 2048;
 constexpr int kQSteps = kQkDim / 16;                               // 36 k-steps of 16
@@ -90,6 +96,14 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// Same, from a wave-uniform base address plus a per-lane 32-bit offset.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N < 63 ? N : 63) : "memory");
@@ -104,6 +118,12 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   const uint32_t lo = __shfl(static_cast<uint32_t>(v), src);
   const uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src);
   return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Value of lane l ^ 32 (the other half of the wave) without going through LDS.
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 // Ancestor-or-self bitmask of node `lane` (lanes >= T get 0) by pointer
@@ -156,9 +176,11 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch L) {
   constexpr int kInstrPerWave = kTileInstr / NW;
   static_assert(kTileInstr % NW == 0, "tile loads must split evenly over the waves");
+  constexpr int kTilesPerWindow = kSlotCap / kKeysPerTile;
 
   __shared__ __attribute__((aligned(1024))) uint8_t kv_s[kStages * kTileBytes];
   __shared__ int32_t slot_s[kSlotCap];
+  __shared__ uint32_t badbits_s[kTilesPerWindow];  // bit k: key k of the tile sits on a bad slot
   __shared__ uint64_t anc_s[kMaxNodes];
   __shared__ int32_t badw_s[NW];
   __shared__ int32_t over_s[NW];
@@ -201,31 +223,28 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   {
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(L.q) +
                          (static_cast<size_t>(b) * L.rows + (row_ok ? row : 0)) * (kQkDim / 8);
-    const bf16x8 zero = {};
 #pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) {
-      const bf16x8 v = qrow[2 * ks + hsel];
-      qf[ks] = row_ok ? v : zero;
-    }
+    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = row_ok ? qrow[2 * ks + hsel] : bf16x8{};
   }
   const int node = row_ok ? row / L.heads : 0;
   const bool need_mask = k1 > ctx;
   uint64_t my_anc = 0;
-  bool win_bad = false;
 
   const uint32_t lds_kv = lds_addr(kv_s);
 
   // Per-lane LDS offsets that do not change from tile to tile.
   const int kkey = lane & 31;
   const int kswz = swz(kkey);
-  int koff[4];
+  int koff[4];  // latent chunks; the rope chunks sit at koff + krope
 #pragma unroll
-  for (int r = 0; r < 4; ++r) koff[r] = kkey * kRowBytes + (((2 * r + hsel) ^ kswz) << 4);
+  for (int r = 0; r < 4; ++r) koff[r] = kkey * kLatentBytes + (((2 * r + hsel) ^ kswz) << 4);
+  const int krope = kRopeBase - kkey * (kLatentBytes - kRopeBytes);
   const int tg = lane >> 4, tj = lane & 15;
   const int vkey = 4 * hsel + (tj >> 2);  // + 16*kk + 8*u
   const int vy = (2 * (tg & 1) + ((tj & 3) >> 1)) ^ swz(vkey);
-  const int voff_even = vkey * kRowBytes + (tj & 1) * 8 + (vy << 4);
-  const int voff_odd = vkey * kRowBytes + (tj & 1) * 8 + ((vy ^ 4) << 4);
+  const int voff_even = vkey * kLatentBytes + (tj & 1) * 8 + (vy << 4);
+  const int voff_odd = vkey * kLatentBytes + (tj & 1) * 8 + ((vy ^ 4) << 4);
+  const uint32_t lane16 = lane * 16;
 
   f32x16 o[kColBlocks];
   float m_ref = -INFINITY;  // reference max (log2 units) of this lane's row
@@ -234,8 +253,164 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   float l_pb = 0.f;         // sum of bf16-rounded weights
   bool overflow = false;    // a score left the range the reference can absorb
 
-  // One pass over the split's keys: windows of up to kSlotCap keys, tiles of
-  // 32 keys streamed through kStages LDS buffers.
+  // ---- building blocks of the tile pipeline
+  // K fragment of k-step ks (dims 16ks..16ks+15 of key lane%32).
+  auto ld_k = [&](const uint8_t* st, int ks) {
+    if (ks < kVDim / 16) return *reinterpret_cast<const bf16x8*>(st + koff[ks & 3] + (ks >> 2) * 128);
+    return *reinterpret_cast<const bf16x8*>(st + koff[ks & 3] + krope);
+  };
+  // One MFMA step of S^T = K Q^T. The accumulator lives in VGPRs (the AGPR
+  // file holds the whole O^T accumulator), so the step is issued as inline
+  // asm with a VGPR destination: back-to-back accumulation into the same
+  // registers needs no wait states; qk_done() adds the 20 wait states an XDL
+  // result needs before a VALU instruction may read it.
+  auto qk_step = [&](f32x16& acc, const bf16x8& a, const bf16x8& q, bool first) {
+    if (first)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(q));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(q));
+  };
+  auto qk_done = [&](f32x16& acc) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc)); };
+  auto qk = [&](const uint8_t* st) {  // S^T of a whole tile, not interleaved
+    f32x16 acc;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) kf[p] = ld_k(st, p);
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
+      if (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st, ks + 4);
+    }
+    qk_done(acc);
+    return acc;
+  };
+
+  // Visibility of the tile's 32 keys for this lane's row: context keys are
+  // visible to every node, a tree key C + j only to the nodes with j in their
+  // ancestor set, keys past the window or on a bad slot to nobody.
+  auto visible_bits = [&](int w0, int wn, int t) -> uint32_t {
+    const int tk0 = t * kKeysPerTile;
+    const int a = w0 + tk0 - ctx;  // key k of the tile is tree node a + k when a + k >= 0
+    const int left = wn - tk0;
+    uint32_t bits = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+    bits &= ~badbits_s[t];
+    uint32_t vis;
+    if (a >= 0) {
+      vis = a < 64 ? static_cast<uint32_t>(my_anc >> a) : 0u;
+    } else if (a > -32) {
+      vis = ((1u << (-a)) - 1u) | static_cast<uint32_t>(my_anc << (-a));
+    } else {
+      vis = 0xffffffffu;
+    }
+    return bits & vis;
+  };
+
+  // Element j of a score tile is key 8*(j/4) + 4*hsel + j%4 of the tile.
+  auto scale_mask = [&](const f32x16& acc, uint32_t vis, float (&tsc)[16]) {
+    const uint32_t vsh = vis >> (4 * hsel);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      tsc[j] = ((vsh >> (8 * (j >> 2) + (j & 3))) & 1u) ? acc[j] * L.scale_log2 : -INFINITY;
+  };
+
+  // Softmax of one tile against the row's reference, cut into 19 pieces so
+  // that it can be spread between the MFMAs of the next tile's scores.
+  // Pieces 0-8: row max; 9: reference; 10-17: weights of two elements each;
+  // 18: sums and the P^T B operands of the two 16-key halves.
+  struct SoftmaxState {
+    float mx, mu, ts, tb;
+    bf16x2 pb2[8];
+  };
+  auto softmax_piece = [&](auto mode_tag, int piece, SoftmaxState& sm, const float (&tsc)[16], bf16x8 (&pf)[2]) {
+    constexpr int kMode = decltype(mode_tag)::value;
+    if (piece == 0) {
+      sm.mx = fmaxf(tsc[0], tsc[1]);
+    } else if (piece < 8) {
+      sm.mx = fmaxf(sm.mx, fmaxf(tsc[2 * piece], tsc[2 * piece + 1]));
+    } else if (piece == 8) {
+      sm.mx = fmaxf(sm.mx, xor32(sm.mx));
+    } else if (piece == 9) {
+      if constexpr (kMode == kPassMaxOnly) {
+        m_max = fmaxf(m_max, sm.mx);
+      } else {
+        if constexpr (kMode == kPassAdaptive) {
+          // The first visible tile fixes the reference. Lifting it by
+          // kRefLift leaves room for scores up to kRefLift + kRefHead above
+          // that tile's max before a weight could overflow.
+          m_ref = (m_ref == -INFINITY && sm.mx > -INFINITY) ? sm.mx + kRefLift : m_ref;
+          overflow |= sm.mx > m_ref + kRefHead;
+        }
+        sm.mu = m_ref == -INFINITY ? 0.f : m_ref;
+        sm.ts = 0.f;
+        sm.tb = 0.f;
+      }
+    } else if (kMode != kPassMaxOnly && piece < 18) {
+      const int k = piece - 10;
+      const float p0 = __builtin_amdgcn_exp2f(tsc[2 * k] - sm.mu);
+      const float p1 = __builtin_amdgcn_exp2f(tsc[2 * k + 1] - sm.mu);
+      sm.ts += p0 + p1;
+      sm.pb2[k] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+      const f32x2 back = __builtin_convertvector(sm.pb2[k], f32x2);
+      sm.tb += back[0] + back[1];
+    } else if (kMode != kPassMaxOnly && piece == 18) {
+      l_sum += sm.ts;
+      l_pb += sm.tb;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pf[kk] = bf16x8{sm.pb2[4 * kk][0], sm.pb2[4 * kk][1], sm.pb2[4 * kk + 1][0], sm.pb2[4 * kk + 1][1],
+                        sm.pb2[4 * kk + 2][0], sm.pb2[4 * kk + 2][1], sm.pb2[4 * kk + 3][0], sm.pb2[4 * kk + 3][1]};
+    }
+  };
+  // Pins the values a piece produced at this point of the instruction stream
+  // (the compiler may not sink the piece past the MFMA that follows).
+  auto anchor = [&](auto mode_tag, int piece, SoftmaxState& sm, bf16x8 (&pf)[2]) {
+    constexpr int kMode = decltype(mode_tag)::value;
+    if (piece <= 8) {
+      asm volatile("" : "+v"(sm.mx));
+    } else if (piece == 9) {
+      if constexpr (kMode != kPassMaxOnly) asm volatile("" : "+v"(sm.mu), "+v"(sm.ts), "+v"(sm.tb));
+    } else if (kMode != kPassMaxOnly && piece < 18) {
+      asm volatile("" : "+v"(sm.ts), "+v"(sm.tb), "+v"(sm.pb2[piece - 10]));
+    } else if (kMode != kPassMaxOnly && piece == 18) {
+      asm volatile("" : "+v"(pf[0]), "+v"(pf[1]));
+    }
+  };
+  auto softmax = [&](auto mode_tag, const float (&tsc)[16], bf16x8 (&pf)[2]) {
+    SoftmaxState sm;
+#pragma unroll
+    for (int piece = 0; piece < 19; ++piece) softmax_piece(mode_tag, piece, sm, tsc, pf);
+  };
+
+  // V^T fragment of PV step i (column block i/2, keys 16*(i%2)..+15).
+  auto ld_v = [&](const uint8_t* st, int i, i16x4 (&v)[2]) {
+    const int cb = i >> 1, kk = i & 1;
+    const uint8_t* vb = st + (cb & 1 ? voff_odd : voff_even) + (cb >> 1) * 128;
+    v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk) * kLatentBytes));
+    v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk + 8) * kLatentBytes));
+  };
+  // O^T += V^T P^T: 32 MFMA steps into the AGPR-resident accumulator, V^T
+  // reads three steps ahead. Issued as inline asm so that the order of loads,
+  // MFMAs and the interleaved VALU work (between(i) after step i) is kept.
+  auto pv = [&](const uint8_t* st, const bf16x8 (&pf)[2], auto&& between) {
+    i16x4 vr[4][2];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) ld_v(st, i, vr[i]);
+#pragma unroll
+    for (int i = 0; i < 2 * kColBlocks; ++i) {
+      if (i + 3 < 2 * kColBlocks) ld_v(st, i + 3, vr[(i + 3) & 3]);
+      const i16x8 v = __builtin_shufflevector(vr[i & 3][0], vr[i & 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(o[i >> 1])
+                   : "v"(__builtin_bit_cast(bf16x8, v)), "v"(pf[i & 1]));
+      between(i);
+    }
+  };
+  auto nothing = [](int) {};
+
+  // One pass over the split's keys: windows of up to kSlotCap keys; tiles of
+  // 32 keys streamed through kStages LDS buffers. Iteration t overlaps the
+  // scores of tile t+1 (MFMA) with the softmax of tile t (VALU), then the PV
+  // product of tile t (MFMA) with the masking of tile t+1's scores (VALU).
   auto run_pass = [&](auto mode_tag) {
     constexpr int kMode = decltype(mode_tag)::value;
     constexpr bool kAccum = kMode != kPassMaxOnly;
@@ -247,17 +422,23 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     }
     for (int w0 = k0; w0 < k1; w0 += kSlotCap) {
       const int wn = min(k1 - w0, kSlotCap);
+      const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
       lds_barrier();  // everyone is done with the previous window or pass
-
-      // Physical slot of every key in this window; -1 marks an out-of-range slot.
+      for (int i = threadIdx.x; i < ntiles; i += NW * 64) badbits_s[i] = 0u;
+      lds_barrier();
+      // Physical slot of every key in this window; bad slots are recorded in
+      // the tile's bad-key bits and loaded from slot 0 instead.
       int bad = 0;
       for (int i = threadIdx.x; i < wn; i += NW * 64) {
         const int p = w0 + i;
         const int page = L.page_table[static_cast<size_t>(b) * L.max_pages + (p >> L.page_shift)];
         const int64_t slot = (static_cast<int64_t>(page) << L.page_shift) + (p & ((1 << L.page_shift) - 1));
         const bool ok = page >= 0 && slot < L.num_slots;
-        slot_s[i] = ok ? static_cast<int32_t>(slot) : -1;
-        bad |= !ok;
+        slot_s[i] = ok ? static_cast<int32_t>(slot) : 0;
+        if (!ok) {
+          atomicOr(&badbits_s[i >> 5], 1u << (i & 31));
+          bad = 1;
+        }
       }
       const int wave_bad = __any(bad);
       if (lane == 0) badw_s[wid] = wave_bad;
@@ -266,127 +447,119 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
         anc_s[lane] = a;
       }
       lds_barrier();
-      win_bad = false;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) win_bad |= badw_s[w] != 0;
       if (kMode == kPassAdaptive) {
+        bool win_bad = false;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) win_bad |= badw_s[w] != 0;
         if (win_bad && threadIdx.x == 0) atomicOr(L.err, MLA_DEVERR_SLOT_RANGE);
         if (need_mask && w0 == k0) my_anc = anc_s[node];
       }
 
-      const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
-
-      auto issue_tile = [&](int t) {
-        const int tk0 = t * kKeysPerTile;
-        const uint32_t base = lds_kv + (t % kStages) * kTileBytes;
-#pragma unroll 3
-        for (int i = 0; i < kInstrPerWave; ++i) {
-          const int ins = wid + i * NW;
-          const int pos = ins * 64 + lane;  // 16-byte chunk position inside the tile
-          const int key = pos / kChunksPerRow;
-          const int c = (pos - key * kChunksPerRow) ^ swz(key);
-          const int kk = min(tk0 + key, wn - 1);  // keys past the window reload a real row
-          int slot = slot_s[kk];
-          slot = slot < 0 ? 0 : slot;
-          const uint8_t* g = L.kv + static_cast<size_t>(slot) * L.kv_row_bytes + c * 16;
-          dma16(g, base + ins * 1024);
+      // Slots behind this wave's loads of tile t: load i is the latent part of
+      // key wid + i*NW (one wave-uniform slot) or, for i*NW + wid >= 32, the
+      // rope parts of eight keys (a slot per lane).
+      auto slot_of = [&](int t, int i) -> int32_t {
+        const int ins = wid + i * NW;
+        const int key = ins < kKeysPerTile ? ins : 8 * (ins - kKeysPerTile) + (lane >> 3);
+        return slot_s[min(t * kKeysPerTile + key, wn - 1)];  // keys past the window reload a real row
+      };
+      auto issue_one = [&](int t, int i, int32_t slot) {
+        const int ins = wid + i * NW;
+        const uint32_t dst = lds_kv + (t % kStages) * kTileBytes;
+        if (ins < kKeysPerTile) {
+          const uint8_t* row = L.kv + static_cast<size_t>(__builtin_amdgcn_readfirstlane(slot)) * L.kv_row_bytes;
+          dma16_sbase(row, lane16 ^ (swz(ins) << 4), dst + ins * kLatentBytes);
+        } else {
+          const int g = ins - kKeysPerTile;
+          const int key = 8 * g + (lane >> 3);
+          const int c = kVDim / 8 + ((lane & 7) ^ swz(key));
+          dma16(L.kv + static_cast<size_t>(slot) * L.kv_row_bytes + c * 16, dst + kRopeBase + g * 1024);
         }
       };
-
+      auto issue_tile = [&](int t) {
+#pragma unroll 3
+        for (int i = 0; i < kInstrPerWave; ++i) issue_one(t, i, slot_of(t, i));
+      };
 #pragma unroll
       for (int t = 0; t < kStages - 1; ++t)
         if (t < ntiles) issue_tile(t);
 
-      for (int t = 0; t < ntiles; ++t) {
-        const int ahead = min(kStages - 2, ntiles - 1 - t);
-        if (ahead >= 2) wait_vmcnt<2 * kInstrPerWave>();
-        else if (ahead == 1) wait_vmcnt<kInstrPerWave>();
+      // Scores of tile 0 (loads complete in issue order: tiles 1 and 2 may
+      // still be in flight).
+      if (ntiles >= 3) wait_vmcnt<2 * kInstrPerWave>();
+      else if (ntiles == 2) wait_vmcnt<kInstrPerWave>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      float tsc[16];
+      scale_mask(qk(kv_s), visible_bits(w0, wn, 0), tsc);
+
+      for (int t = 0; t + 1 < ntiles; ++t) {
+        // Tile t+1 has landed (this wave's part) once only tiles issued after
+        // it are outstanding; the barrier also retires PV(t-1), freeing the
+        // stage that tile t+3 loads into.
+        if (t + 2 < ntiles) wait_vmcnt<kInstrPerWave>();
         else wait_vmcnt<0>();
         lds_barrier();
-        if (t + kStages - 1 < ntiles) issue_tile(t + kStages - 1);
-
+        const bool dma_next = t + 3 < ntiles;
         const uint8_t* st = kv_s + (t % kStages) * kTileBytes;
-        const int tk0 = t * kKeysPerTile;
+        const uint8_t* st1 = kv_s + ((t + 1) % kStages) * kTileBytes;
 
-        // ---- S^T = K Q^T for 32 keys x this wave's 32 rows
-        f32x16 sacc = {};
+        // phase 1: the 36 MFMAs of QK(t+1) with K fragments prefetched four
+        // steps ahead; between them the softmax of tile t (VALU) and the loads
+        // of tile t+3, spread over the chain (load i after step i*E + E-1,
+        // its slot read from LDS three steps earlier).
+        bf16x8 pf[2];
+        {
+          f32x16 acc;
+          bf16x8 kf[4];
+          SoftmaxState sm;
+          constexpr int kDmaEvery = kQSteps / kInstrPerWave;
+          constexpr int kSlotLead = 3;
+          int32_t slr[4];
 #pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + koff[ks & 3] + (ks >> 2) * 128);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
-          if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // Element j of sacc is key tk0 + 8*(j/4) + 4*hsel + j%4 of row lane%32.
-        float tsc[16];
+          for (int i = 0; i < kInstrPerWave && i * kDmaEvery + kDmaEvery - 1 < kSlotLead; ++i)
+            if (dma_next) slr[i & 3] = slot_of(t + 3, i);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) tsc[j] = sacc[j] * L.scale_log2;
-        const bool special = (w0 + tk0 + kKeysPerTile > ctx) || (tk0 + kKeysPerTile > wn) || win_bad;
-        if (special) {
+          for (int p = 0; p < 4; ++p) kf[p] = ld_k(st1, p);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = tk0 + 8 * (j >> 2) + 4 * hsel + (j & 3);
-            bool vis = key < wn;
-            if (vis) {
-              vis = slot_s[key] >= 0;
-              const int p = w0 + key;
-              if (p >= ctx) vis = vis && ((my_anc >> (p - ctx)) & 1ull);
+          for (int ks = 0; ks < kQSteps; ++ks) {
+            qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
+            if (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st1, ks + 4);
+            if (ks < 19) {
+              softmax_piece(mode_tag, ks, sm, tsc, pf);
+              anchor(mode_tag, ks, sm, pf);
             }
-            tsc[j] = vis ? tsc[j] : -INFINITY;
-          }
-        }
-        float mt = tsc[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) mt = fmaxf(mt, tsc[j]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        if constexpr (kMode == kPassMaxOnly) {
-          m_max = fmaxf(m_max, mt);
-        } else {
-          if constexpr (kMode == kPassAdaptive) {
-            // The first visible tile fixes the reference. Lifting it by
-            // kRefLift leaves room for scores up to kRefLift + kRefHead above
-            // that tile's max before a weight could overflow.
-            if (m_ref == -INFINITY && mt > -INFINITY) m_ref = mt + kRefLift;
-            overflow |= mt > m_ref + kRefHead;
-          }
-          const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-          float ps[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) ps[j] = __builtin_amdgcn_exp2f(tsc[j] - mu);
-
-          bf16x2 pb2[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) pb2[k] = __builtin_convertvector(f32x2{ps[2 * k], ps[2 * k + 1]}, bf16x2);
-          float ts = 0.f, tb = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) ts += ps[j];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const f32x2 back = __builtin_convertvector(pb2[k], f32x2);
-            tb += back[0] + back[1];
-          }
-          l_sum += ts;
-          l_pb += tb;
-          bf16x8 pf[2];
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            pf[kk] = bf16x8{pb2[4 * kk][0], pb2[4 * kk][1], pb2[4 * kk + 1][0], pb2[4 * kk + 1][1],
-                            pb2[4 * kk + 2][0], pb2[4 * kk + 2][1], pb2[4 * kk + 3][0], pb2[4 * kk + 3][1]};
-
-          // ---- O^T += V^T P^T; V^T fragments via transposing LDS reads
-#pragma unroll
-          for (int cb = 0; cb < kColBlocks; ++cb) {
-            const uint8_t* vb = st + (cb & 1 ? voff_odd : voff_even) + (cb >> 1) * 128;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-              const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk) * kRowBytes));
-              const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk + 8) * kRowBytes));
-              const i16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-              o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf[kk], o[cb], 0, 0, 0);
+            if (dma_next) {
+              const int ahead = ks + kSlotLead;  // step whose load needs its slot now
+              if (ahead < kQSteps && ahead % kDmaEvery == kDmaEvery - 1)
+                slr[(ahead / kDmaEvery) & 3] = slot_of(t + 3, ahead / kDmaEvery);
+              if (ks % kDmaEvery == kDmaEvery - 1) issue_one(t + 3, ks / kDmaEvery, slr[(ks / kDmaEvery) & 3]);
             }
-            if (cb & 1) __builtin_amdgcn_sched_barrier(0);
+          }
+          qk_done(acc);
+
+          // phase 2: PV(t) on the matrix cores; the masking of tile t+1's
+          // scores (one element per step) on the VALU in between.
+          const uint32_t vsh = visible_bits(w0, wn, t + 1) >> (4 * hsel);
+          auto mask_step = [&](int i) {
+            if (i < 16) {
+              tsc[i] = ((vsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? acc[i] * L.scale_log2 : -INFINITY;
+              asm volatile("" : "+v"(tsc[i]));
+            }
+          };
+          if constexpr (kAccum) {
+            pv(st, pf, mask_step);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mask_step(i);
           }
         }
+      }
+      // last tile of the window
+      {
+        bf16x8 pf[2];
+        softmax(mode_tag, tsc, pf);
+        if constexpr (kAccum) pv(kv_s + ((ntiles - 1) % kStages) * kTileBytes, pf, nothing);
       }
     }
   };
@@ -405,9 +578,12 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   }
 
   // ---- partial result of this split: O / l (fp32) and lse in log2 units
+  // (wait states between the last XDL write of O and the reads below)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
   const float l_sum_t = l_sum + __shfl_xor(l_sum, 32);
   const float l_pb_t = l_pb + __shfl_xor(l_pb, 32);
   if (lane < 32) *lse_dst = l_sum_t > 0.f ? m_ref + __builtin_amdgcn_logf(l_sum_t) : -INFINITY;
+  if (!row_ok) return;  // padding rows are never read
   const float inv = l_pb_t > 0.f ? 1.f / l_pb_t : 0.f;
   f32x4* dst = reinterpret_cast<f32x4*>(L.part_o) +
                ((static_cast<size_t>(b) * L.nsplit + s) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
@@ -422,19 +598,19 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     }
 }
 
-// Merge of the split partials of one fragment slot (32 rows x 8 columns): the
-// four waves of the workgroup take every fourth split, so a slot's partials
-// are read with four waves' worth of loads in flight. Pass 1 finds each row's
-// largest partial lse M; pass 2 accumulates w_s = 2^(lse_s - M) and w_s * O_s
-// (empty splits have lse = -inf and are skipped); the waves' sums are added in
-// LDS. out = sum w_s O_s / sum w_s rounded to bf16 once; lse = M + log2 sum w_s,
-// converted to natural-log units.
-constexpr int kCombineWaves = 4;
+// Merge of the split partials of one fragment slot (32 rows x 8 columns). The
+// kCombineWaves waves of the workgroup take every kCombineWaves-th split and
+// keep a running merge per lane (its row, four columns): M = largest lse so
+// far, acc = sum 2^(lse_s - M) O_s, w = sum 2^(lse_s - M), rescaled when M
+// grows; empty splits (lse = -inf) are skipped. The waves' states are merged
+// the same way in LDS. out = acc / w rounded to bf16 once; lse = M + log2 w in
+// natural-log units.
+constexpr int kCombineWaves = 8;
 
 __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(VerifyLaunch L) {
-  __shared__ float red_m[kCombineWaves][32];
   __shared__ f32x4 red_acc[kCombineWaves][64];
   __shared__ float red_w[kCombineWaves][64];
+  __shared__ float red_m[kCombineWaves][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int nwb = L.rows_pad / 32;
@@ -442,42 +618,44 @@ __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(Veri
   const int wb = (blockIdx.x >> 6) % nwb;
   const int b = (blockIdx.x >> 6) / nwb;
   const int row = wb * 32 + (lane & 31);  // < rows_pad: its partial lse is always written
+  const bool row_ok = row < L.rows;       // partial outputs exist for real rows only
 
   const float* pl = L.part_lse + static_cast<size_t>(b) * L.nsplit * L.rows_pad + row;
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int s = w; s < L.nsplit; s += kCombineWaves) mx = fmaxf(mx, pl[static_cast<size_t>(s) * L.rows_pad]);
-  if (lane < 32) red_m[w][lane] = mx;
-  __syncthreads();
-  mx = red_m[0][lane & 31];
-#pragma unroll
-  for (int i = 1; i < kCombineWaves; ++i) mx = fmaxf(mx, red_m[i][lane & 31]);
-
+  const size_t split_stride = static_cast<size_t>(nwb) * 4096;
+  const f32x4* po = reinterpret_cast<const f32x4*>(L.part_o) + static_cast<size_t>(b) * L.nsplit * split_stride +
+                    static_cast<size_t>(wb) * 4096 + frag * 64 + lane;
+  float mx = -INFINITY, wsum = 0.f;
   f32x4 acc = {};
-  float wsum = 0.f;
-  if (mx > -INFINITY) {
-    const size_t split_stride = static_cast<size_t>(nwb) * 4096;
-    const f32x4* po = reinterpret_cast<const f32x4*>(L.part_o) +
-                      static_cast<size_t>(b) * L.nsplit * split_stride + static_cast<size_t>(wb) * 4096 +
-                      frag * 64 + lane;
-#pragma unroll 8
-    for (int s = w; s < L.nsplit; s += kCombineWaves) {
-      const float l2 = pl[static_cast<size_t>(s) * L.rows_pad];
-      const f32x4 v = po[s * split_stride];
-      const bool live = l2 > -INFINITY;
-      const float wt = live ? __builtin_amdgcn_exp2f(l2 - mx) : 0.f;
-      acc += wt * (live ? v : f32x4{});
-      wsum += wt;
-    }
+#pragma unroll 16
+  for (int s = w; s < L.nsplit; s += kCombineWaves) {
+    const float l2 = pl[static_cast<size_t>(s) * L.rows_pad];
+    const bool live = row_ok && l2 > -INFINITY;
+    const f32x4 v = row_ok ? po[s * split_stride] : f32x4{};
+    const float nm = live ? fmaxf(mx, l2) : mx;
+    const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - nm);
+    const float wt = live ? __builtin_amdgcn_exp2f(l2 - nm) : 0.f;
+    acc = acc * sc + wt * (live ? v : f32x4{});
+    wsum = wsum * sc + wt;
+    mx = nm;
   }
   red_acc[w][lane] = acc;
   red_w[w][lane] = wsum;
+  red_m[w][lane] = mx;
   __syncthreads();
-  if (w != 0 || row >= L.rows) return;
+  if (w != 0 || !row_ok) return;
+  float m_all = red_m[0][lane];
 #pragma unroll
-  for (int i = 1; i < kCombineWaves; ++i) {
-    acc += red_acc[i][lane];
-    wsum += red_w[i][lane];
+  for (int i = 1; i < kCombineWaves; ++i) m_all = fmaxf(m_all, red_m[i][lane]);
+  acc = f32x4{};
+  wsum = 0.f;
+  if (m_all > -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < kCombineWaves; ++i) {
+      const float mi = red_m[i][lane];
+      const float sc = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - m_all);
+      acc += sc * red_acc[i][lane];
+      wsum += sc * red_w[i][lane];
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const f32x4 r = acc * inv;
@@ -489,7 +667,7 @@ __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(Veri
   *dst = bf16x4{lo[0], lo[1], hi[0], hi[1]};
   if (frag == 0 && lane < 32)
     L.lse[static_cast<size_t>(b) * L.rows + row] =
-        wsum > 0.f ? (mx + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f : -INFINITY;
+        wsum > 0.f ? (m_all + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f : -INFINITY;
 }
 
 }  // namespace
