@@ -97,9 +97,14 @@ def default_nsplit(batch, nodes, heads, max_keys) -> int:
 # ---------------------------------------------------------------- inputs on the GPU
 
 class Replicated:
-    """R replicas of one logical workload in disjoint pool regions."""
+    """R replicas of one logical workload in one pool of R x (pages per
+    replica) pages. "scattered": one random permutation of all the pool's
+    pages, so every replica's pages lie all over the pool (page size 1 is a
+    KV row per page, the fragmented layout). "contiguous": replica r owns a
+    run of consecutive pages, in logical order (a defragmented pool)."""
 
-    def __init__(self, torch, logical_rows, q_bits, seq_lens, tree_parent, page_size, replicas, seed):
+    def __init__(self, torch, logical_rows, q_bits, seq_lens, tree_parent, page_size, replicas, seed,
+                 layout="scattered"):
         self.torch = torch
         dev = "cuda"
         b = len(seq_lens)
@@ -119,9 +124,15 @@ class Replicated:
             off += n
         self.pool = torch.empty((replicas * ptot * ps, QK_DIM), dtype=torch.bfloat16, device=dev)
         pool_pages = self.pool.view(replicas * ptot, ps, QK_DIM)
+        if layout == "contiguous":
+            order = torch.arange(replicas * ptot, device=dev)
+        elif layout == "scattered":
+            order = torch.randperm(replicas * ptot, generator=gen, device=dev)
+        else:
+            raise ValueError(f"unknown layout {layout}")
         self.page_tables = []
         for r in range(replicas):
-            perm = torch.randperm(ptot, generator=gen, device=dev) + r * ptot
+            perm = order[r * ptot:(r + 1) * ptot]
             pool_pages[perm] = padded.view(ptot, ps, QK_DIM)
             pt = torch.full((b, self.max_pages), -1, dtype=torch.int32, device=dev)
             o = 0
@@ -135,6 +146,17 @@ class Replicated:
         self.tree_parent = torch.tensor(np.asarray(tree_parent, dtype=np.int32), device=dev)
         self.page_size = ps
         self.replicas = replicas
+        self.layout = layout
+
+
+def case_layout(case) -> str:
+    """'contiguous' when every request's pages are consecutive ascending ids."""
+    for b in range(case.batch):
+        n_pages = math.ceil(int(case.seq_lens[b]) / case.page_size)
+        row = case.page_table[b, :n_pages].astype(np.int64)
+        if n_pages > 1 and not np.all(np.diff(row) == 1):
+            return "scattered"
+    return "contiguous"
 
 
 def bf16_from_bits(torch, bits):
@@ -276,15 +298,17 @@ def measure_case(torch, mv, case, nsplit, steps, warmup, seed):
     q = bf16_from_bits(torch, case.q).cuda()
     kvb = kv_bytes(case.seq_lens)
     replicas = max(1, math.ceil(ROTATE_BYTES / max(kvb, 1)))
-    rep = Replicated(torch, lr, q, case.seq_lens, case.tree_parent, case.page_size, replicas, seed)
+    rep = Replicated(torch, lr, q, case.seq_lens, case.tree_parent, case.page_size, replicas, seed,
+                     layout=case_layout(case))
     del lr
     res = time_workload(torch, mv, rep, case.num_nodes, case.num_heads, nsplit, case.sm_scale, steps, warmup)
     return res, rep
 
 
-def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None):
+def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None, layout="scattered"):
     """A context-sweep point generated on the GPU (seeded): N(0,1) bf16 rows,
-    uniform-parent tree (depth <= 8 for 32 nodes), page size 1."""
+    uniform-parent tree (depth <= 8 for 32 nodes), page size 1, KV rows
+    scattered over the pool or contiguous."""
     from workloads.gen import tree_depth_capped, tree_uniform
 
     rng = np.random.default_rng(seed + context + nodes)
@@ -296,7 +320,7 @@ def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None):
     q = torch.randn((1, nodes, heads, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     kvb = kv_bytes([n])
     replicas = max(1, math.ceil(ROTATE_BYTES / kvb))
-    rep = Replicated(torch, rows, q, [n], tree[None, :], 1, replicas, seed)
+    rep = Replicated(torch, rows, q, [n], tree[None, :], 1, replicas, seed, layout=layout)
     del rows
     nsplit = nsplit or default_nsplit(1, nodes, heads, n)
     steps = replicas * max(2, 64 // replicas)
@@ -306,7 +330,8 @@ def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None):
     eff = kvb / (lat_us * 1e-6) / 1e9
     pbytes = partial_algorithmic_bytes([n], nodes, heads, 1)
     flops = algorithmic_flops([n], nodes, heads)
-    entry = dict(workload=f"context {context}, {nodes}-node tree, {heads} heads, page size 1",
+    entry = dict(workload=f"context {context}, {nodes}-node tree, {heads} heads, page size 1, {layout} KV rows",
+                 layout=layout,
                  context=context, nodes=nodes, rows=nodes * heads, nsplit=nsplit, replicas=replicas,
                  latency_us=round(lat_us, 2), eff_kv_gbs=round(eff, 1), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
                  partial_us=round(partial_us, 2),
@@ -324,7 +349,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--workload", default="C2",
-                    help="C1, C2, C3, C4a, C4b, C5, or a context-sweep point S<context>_T<nodes>")
+                    help="C1, C2, C3, C4a, C4b, C5, or a context-sweep point S<context>_T<nodes>[_contig]")
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -343,8 +368,10 @@ def main():
 
     mv.load_library()
     if args.workload.startswith("S"):
-        ctx, nodes = args.workload[1:].split("_T")
-        e = sweep_point(torch, mv, int(ctx), int(nodes), nsplit=args.nsplit)
+        spec = args.workload[1:].split("_")
+        ctx, nodes = int(spec[0]), int(spec[1][1:])
+        layout = "contiguous" if spec[2:] == ["contig"] else "scattered"
+        e = sweep_point(torch, mv, ctx, nodes, nsplit=args.nsplit, layout=layout)
         log(json.dumps(e))
         print(json.dumps(dict(metric=METRIC, value=e["eff_kv_gbs"], unit="GB/s", n_gpus=1, latency_us=e["latency_us"],
                               config=dict(workload=e["workload"]), sweep=[e])), flush=True)
@@ -376,6 +403,7 @@ def main():
                 flops_per_launch=pflops)
     gpu_out = out.view(torch.int16).cpu().numpy().view(np.uint16)
     gpu_lse = lse.cpu().numpy()
+    layout = rep.layout
     del rep, out, lse, ws
     torch.cuda.empty_cache()
 
@@ -385,7 +413,8 @@ def main():
                 config=dict(workload=f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
                             context=case.meta["context"], nodes=case.num_nodes, heads=case.num_heads,
                             page_size=case.page_size, nsplit=nsplit, rows=case.num_nodes * case.num_heads,
-                            replicas=math.ceil(ROTATE_BYTES / kvb), parallelism="none (1 GPU)"),
+                            replicas=math.ceil(ROTATE_BYTES / kvb), layout=layout,
+                            parallelism="none (1 GPU)"),
                 latency_us=round(lat_us, 3), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
                 roofline=roof, device_error=dev_err)
 

@@ -16,8 +16,11 @@
 //    A tile holds the 32 latent parts (1 KiB each, one wave-wide load per key
 //    whose row address is wave-uniform) followed by the 32 rope parts (128 B,
 //    eight keys per load). Each 16-byte chunk lands at chunk ^ swz(key)
-//    inside its 128-byte group so both LDS read patterns below are free of
-//    bank conflicts.
+//    inside its 128-byte group, which spreads the fragment reads below over
+//    the LDS banks with addresses that are a per-lane base plus an immediate.
+//  * The loop over tiles is straight-line code: the loads of tile t+3 are
+//    issued between the MFMAs of tile t+1 with no branch (the last two steps,
+//    which issue none, are a loop of their own).
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K fragments come from LDS, the wave's 32 query rows stay in VGPRs for the
 //    whole kernel. In the S^T accumulator every lane owns one query row, so the
@@ -45,6 +48,8 @@
 // empty splits, no device-to-host traffic, no allocation.
 
 #include <hip/hip_runtime.h>
+
+#include <utility>
 #include <math.h>
 #include <stdint.h>
 
@@ -79,9 +84,12 @@ constexpr int kColBlocks = kVDim / 32;                             // 16
 constexpr float kRefLift = 32.0f;  // log2 units: reference above the first visible tile max
 constexpr float kRefHead = 96.0f;  // log2 units: largest weight kept is 2^kRefHead
 
-// Chunk permutation inside a 128-byte group, keyed by the key's index in the
-// tile: 8 consecutive keys hit 8 distinct 16-byte slots (K reads), and the
-// 32-byte pairs of 4 consecutive keys hit 4 distinct pairs (V^T reads).
+// 16-byte chunk permutation inside a 128-byte group, keyed by the key's index
+// in the tile: 8 consecutive keys hit 8 distinct slots (K reads), and the
+// 32-byte pairs of 4 consecutive keys hit 4 distinct pairs (V^T reads). A
+// 256-byte permutation measures faster for the V^T reads alone (gfx950 LDS
+// serves ds_read_b64_tr_b16 256 bytes wide) but its fragment addresses cost
+// a VALU operation per read, which costs more in this loop than it saves.
 __device__ __forceinline__ int swz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -103,6 +111,22 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
+
+// f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{}): a
+// loop whose index is a compile-time constant in every copy of the body.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -276,11 +300,11 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     bf16x8 kf[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) kf[p] = ld_k(st, p);
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) {
+    static_for<kQSteps>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
       qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
-      if (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st, ks + 4);
-    }
+      if constexpr (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st, ks + 4);
+    });
     qk_done(acc);
     return acc;
   };
@@ -294,14 +318,13 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     const int left = wn - tk0;
     uint32_t bits = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
     bits &= ~badbits_s[t];
-    uint32_t vis;
-    if (a >= 0) {
-      vis = a < 64 ? static_cast<uint32_t>(my_anc >> a) : 0u;
-    } else if (a > -32) {
-      vis = ((1u << (-a)) - 1u) | static_cast<uint32_t>(my_anc << (-a));
-    } else {
-      vis = 0xffffffffu;
-    }
+    // Keys before the tree (a + k < 0) are visible; node j = a + k is visible
+    // when bit j of the ancestor mask is set. Selects, not branches: the
+    // shifts are clamped to [0, 63] and the out-of-range cases chosen after.
+    const uint64_t ctx_then_anc = (my_anc << 32) | 0xffffffffull;
+    const uint32_t v_lo = static_cast<uint32_t>(ctx_then_anc >> min(max(a + 32, 0), 63));
+    const uint32_t v_hi = static_cast<uint32_t>(my_anc >> min(max(a, 0), 63));
+    const uint32_t vis = a < 0 ? (a <= -32 ? 0xffffffffu : v_lo) : (a < 64 ? v_hi : 0u);
     return bits & vis;
   };
 
@@ -337,7 +360,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
           // The first visible tile fixes the reference. Lifting it by
           // kRefLift leaves room for scores up to kRefLift + kRefHead above
           // that tile's max before a weight could overflow.
-          m_ref = (m_ref == -INFINITY && sm.mx > -INFINITY) ? sm.mx + kRefLift : m_ref;
+          // (-inf + kRefLift stays -inf: a fully masked tile leaves it unset)
+          m_ref = m_ref == -INFINITY ? sm.mx + kRefLift : m_ref;
           overflow |= sm.mx > m_ref + kRefHead;
         }
         sm.mu = m_ref == -INFINITY ? 0.f : m_ref;
@@ -381,15 +405,17 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     for (int piece = 0; piece < 19; ++piece) softmax_piece(mode_tag, piece, sm, tsc, pf);
   };
 
-  // V^T fragment of PV step i (column block i/2, keys 16*(i%2)..+15).
+  // V^T fragment of PV step i (column block i%16, keys 16*(i/16)..+15).
   auto ld_v = [&](const uint8_t* st, int i, i16x4 (&v)[2]) {
-    const int cb = i >> 1, kk = i & 1;
+    const int cb = i % kColBlocks, kk = i / kColBlocks;
     const uint8_t* vb = st + (cb & 1 ? voff_odd : voff_even) + (cb >> 1) * 128;
     v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk) * kLatentBytes));
     v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk + 8) * kLatentBytes));
   };
   // O^T += V^T P^T: 32 MFMA steps into the AGPR-resident accumulator, V^T
-  // reads three steps ahead. Issued as inline asm so that the order of loads,
+  // reads three steps ahead. Keys 0-15 of the tile go into all 16 column
+  // blocks before keys 16-31, so no MFMA waits for the one before it (a
+  // dependent MFMA issues only after its predecessor has finished). Issued as inline asm so that the order of loads,
   // MFMAs and the interleaved VALU work (between(i) after step i) is kept.
   auto pv = [&](const uint8_t* st, const bf16x8 (&pf)[2], auto&& between) {
     i16x4 vr[4][2];
@@ -400,8 +426,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       if (i + 3 < 2 * kColBlocks) ld_v(st, i + 3, vr[(i + 3) & 3]);
       const i16x8 v = __builtin_shufflevector(vr[i & 3][0], vr[i & 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                   : "+a"(o[i >> 1])
-                   : "v"(__builtin_bit_cast(bf16x8, v)), "v"(pf[i & 1]));
+                   : "+a"(o[i % kColBlocks])
+                   : "v"(__builtin_bit_cast(bf16x8, v)), "v"(pf[i / kColBlocks]));
       between(i);
     }
   };
@@ -458,22 +484,37 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       // Slots behind this wave's loads of tile t: load i is the latent part of
       // key wid + i*NW (one wave-uniform slot) or, for i*NW + wid >= 32, the
       // rope parts of eight keys (a slot per lane).
+      // Load i of this wave for a tile: the latent part of one key (a 1 KiB
+      // row, one slot for the whole wave) or the rope parts of eight keys.
+      // The assignment makes every load of NW = 1, 2, 4 and all but load 10
+      // of NW = 3 the same kind on every wave, so that, with i known after
+      // unrolling, the kind is a compile-time constant.
+      auto ins_of = [&](int i) -> int {
+        if constexpr (NW == 3)
+          return i < 10 ? wid + 3 * i : (i == 10 ? (wid < 2 ? 30 + wid : kKeysPerTile + 3) : kKeysPerTile + wid);
+        else
+          return wid + i * NW;
+      };
       auto slot_of = [&](int t, int i) -> int32_t {
-        const int ins = wid + i * NW;
+        const int ins = ins_of(i);
         const int key = ins < kKeysPerTile ? ins : 8 * (ins - kKeysPerTile) + (lane >> 3);
         return slot_s[min(t * kKeysPerTile + key, wn - 1)];  // keys past the window reload a real row
       };
       auto issue_one = [&](int t, int i, int32_t slot) {
-        const int ins = wid + i * NW;
-        const uint32_t dst = lds_kv + (t % kStages) * kTileBytes;
-        if (ins < kKeysPerTile) {
+        const int ins = ins_of(i);  // wave-uniform
+        const uint32_t stage = lds_kv + (t % kStages) * kTileBytes;
+        const bool all_latent = NW == 3 ? i < 10 : i < kKeysPerTile / NW;
+        if (all_latent) {  // row address in SGPRs, lane offset in a VGPR
           const uint8_t* row = L.kv + static_cast<size_t>(__builtin_amdgcn_readfirstlane(slot)) * L.kv_row_bytes;
-          dma16_sbase(row, lane16 ^ (swz(ins) << 4), dst + ins * kLatentBytes);
-        } else {
+          dma16_sbase(row, lane16 ^ (swz(ins) << 4), stage + ins * kLatentBytes);
+        } else {  // rope parts, or (NW = 3, load 10) either kind: selects, not branches
+          const bool latent = ins < kKeysPerTile;
           const int g = ins - kKeysPerTile;
-          const int key = 8 * g + (lane >> 3);
-          const int c = kVDim / 8 + ((lane & 7) ^ swz(key));
-          dma16(L.kv + static_cast<size_t>(slot) * L.kv_row_bytes + c * 16, dst + kRopeBase + g * 1024);
+          const int rkey = 8 * g + (lane >> 3);
+          const uint32_t chunk =
+              latent ? (lane16 ^ (swz(ins) << 4)) : ((kVDim / 8 + ((lane & 7) ^ swz(rkey))) << 4);
+          const uint32_t dst = stage + (latent ? ins * kLatentBytes : kRopeBase + g * 1024);
+          dma16(L.kv + static_cast<size_t>(static_cast<uint32_t>(slot)) * L.kv_row_bytes + chunk, dst);
         }
       };
       auto issue_tile = [&](int t) {
@@ -493,14 +534,17 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       float tsc[16];
       scale_mask(qk(kv_s), visible_bits(w0, wn, 0), tsc);
 
-      for (int t = 0; t + 1 < ntiles; ++t) {
+      // Step t: scores of tile t+1, softmax and PV of tile t, loads of tile
+      // t+3. The steps that issue loads and the last two (which issue none)
+      // are separate loops, so the steady state has no branches.
+      auto step = [&](auto dma_tag, int t) {
+        constexpr bool dma_next = decltype(dma_tag)::value;
         // Tile t+1 has landed (this wave's part) once only tiles issued after
         // it are outstanding; the barrier also retires PV(t-1), freeing the
         // stage that tile t+3 loads into.
-        if (t + 2 < ntiles) wait_vmcnt<kInstrPerWave>();
+        if (dma_next || t + 2 < ntiles) wait_vmcnt<kInstrPerWave>();
         else wait_vmcnt<0>();
         lds_barrier();
-        const bool dma_next = t + 3 < ntiles;
         const uint8_t* st = kv_s + (t % kStages) * kTileBytes;
         const uint8_t* st1 = kv_s + ((t + 1) % kStages) * kTileBytes;
 
@@ -518,24 +562,25 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
           int32_t slr[4];
 #pragma unroll
           for (int i = 0; i < kInstrPerWave && i * kDmaEvery + kDmaEvery - 1 < kSlotLead; ++i)
-            if (dma_next) slr[i & 3] = slot_of(t + 3, i);
+            if constexpr (dma_next) slr[i & 3] = slot_of(t + 3, i);
 #pragma unroll
           for (int p = 0; p < 4; ++p) kf[p] = ld_k(st1, p);
-#pragma unroll
-          for (int ks = 0; ks < kQSteps; ++ks) {
+          static_for<kQSteps>([&](auto ks_c) {
+            constexpr int ks = decltype(ks_c)::value;
             qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
-            if (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st1, ks + 4);
-            if (ks < 19) {
+            if constexpr (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st1, ks + 4);
+            if constexpr (ks < 19) {
               softmax_piece(mode_tag, ks, sm, tsc, pf);
               anchor(mode_tag, ks, sm, pf);
             }
-            if (dma_next) {
-              const int ahead = ks + kSlotLead;  // step whose load needs its slot now
-              if (ahead < kQSteps && ahead % kDmaEvery == kDmaEvery - 1)
+            if constexpr (dma_next) {
+              constexpr int ahead = ks + kSlotLead;  // step whose load needs its slot now
+              if constexpr (ahead < kQSteps && ahead % kDmaEvery == kDmaEvery - 1)
                 slr[(ahead / kDmaEvery) & 3] = slot_of(t + 3, ahead / kDmaEvery);
-              if (ks % kDmaEvery == kDmaEvery - 1) issue_one(t + 3, ks / kDmaEvery, slr[(ks / kDmaEvery) & 3]);
+              if constexpr (ks % kDmaEvery == kDmaEvery - 1)
+                issue_one(t + 3, ks / kDmaEvery, slr[(ks / kDmaEvery) & 3]);
             }
-          }
+          });
           qk_done(acc);
 
           // phase 2: PV(t) on the matrix cores; the masking of tile t+1's
@@ -554,7 +599,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
             for (int i = 0; i < 16; ++i) mask_step(i);
           }
         }
-      }
+      };
+      int t = 0;
+      for (; t + 3 < ntiles; ++t) step(BoolTag<true>{}, t);
+      for (; t + 1 < ntiles; ++t) step(BoolTag<false>{}, t);
       // last tile of the window
       {
         bf16x8 pf[2];
