@@ -10,8 +10,9 @@ sit in disjoint regions of one pool (R x KV bytes >= 1 GiB); every replica
 holds the same logical rows, so every step computes the same result. The R
 calls are captured in one hipGraph and replayed.
 
-Prints one JSON line. Options: --workload (C1, C2, C3, C4a, C4b, C5),
---nsplit, --steps, --warmup, --no-sweep, --no-cpu.
+Prints one JSON line. Options: --workload (C1, C2, C3, C4a, C4b, C5, or a
+sweep point S<context>_T<nodes>[_contig]), --nsplit, --steps, --warmup,
+--no-sweep, --full-sweep, --no-cpu.
 """
 
 from __future__ import annotations
@@ -36,6 +37,12 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 QK_DIM, V_DIM = 576, 512
 KV_ROW_BYTES = QK_DIM * 2  # one bf16 latent row per key
 ROTATE_BYTES = 1 << 30     # >= 4 x the 256 MB Infinity Cache
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_mla_amd", "csrc", "mla_verify_kernels.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "verify_partial_C2_hbm_traffic.md")
+# Context-sweep grid (contexts x tree sizes); --full-sweep adds the short contexts.
+SWEEP = [(c, t) for c in (4_096, 16_384, 65_536, 131_072, 184_728) for t in (9, 16, 32)]
+FULL_SWEEP = [(c, t) for c in (1_024, 2_048, 4_096, 8_192, 16_384, 32_768, 65_536, 131_072, 184_728)
+              for t in (9, 16, 32)]
 
 WORKLOAD_TEXT = {
     "C1": "1 request, context 256, 4-node chain, 8 heads, page size 1",
@@ -56,6 +63,12 @@ def log(msg: str):
 def kv_bytes(seq_lens) -> int:
     """Latent bytes a verify call must read: one 1,152-byte row per key."""
     return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * KV_ROW_BYTES
+
+
+def effective_kv_gbs(seq_lens, seconds: float) -> float:
+    """The metric's effective KV bandwidth: latent bytes a step must read over
+    the step time, in GB/s."""
+    return kv_bytes(seq_lens) / seconds / 1e9
 
 
 def partial_algorithmic_bytes(seq_lens, nodes, heads, page_size) -> int:
@@ -92,6 +105,31 @@ def default_nsplit(batch, nodes, heads, max_keys) -> int:
     want_wgs = 256
     per_req = max(1, want_wgs // max(1, batch * row_blocks))
     return int(max(1, min(per_req, max_keys // 256 if max_keys >= 256 else 1)))
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel
+    calibration). Returns None unless the summary was taken on this workload
+    from the kernel source as it is now."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            fields = dict(ln.split(":", 1) for ln in f if ln.startswith(("traffic_", "kernel_source_sha256", "workload")))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("kernel_source_sha256") != kernel_source_digest() or fields.get("workload") != workload:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------- inputs on the GPU
@@ -327,7 +365,7 @@ def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None, layout=
     ms, partial_us, *_ = time_workload(torch, mv, rep, nodes, heads, nsplit, 1.0 / math.sqrt(192.0), steps,
                                        replicas)
     lat_us = ms * 1e3
-    eff = kvb / (lat_us * 1e-6) / 1e9
+    eff = effective_kv_gbs([n], lat_us * 1e-6)
     pbytes = partial_algorithmic_bytes([n], nodes, heads, 1)
     flops = algorithmic_flops([n], nodes, heads)
     entry = dict(workload=f"context {context}, {nodes}-node tree, {heads} heads, page size 1, {layout} KV rows",
@@ -352,6 +390,7 @@ def main():
                     help="C1, C2, C3, C4a, C4b, C5, or a context-sweep point S<context>_T<nodes>[_contig]")
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--full-sweep", action="store_true", help="contexts from 1k to 184,728 (27 points)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=1234)
     args = ap.parse_args()
@@ -387,18 +426,19 @@ def main():
     dev_err = mv.device_error(ws)
     lat_us = ms * 1e3
     kvb = kv_bytes(case.seq_lens)
-    eff = kvb / (lat_us * 1e-6) / 1e9
+    eff = effective_kv_gbs(case.seq_lens, lat_us * 1e-6)
     bound = roof_bound(case.num_nodes, case.num_heads)
     pbytes = partial_algorithmic_bytes(case.seq_lens, case.num_nodes, case.num_heads, case.page_size)
     pflops = algorithmic_flops(case.seq_lens, case.num_nodes, case.num_heads)
+    traffic = measured_traffic(args.workload)
     if bound == "hbm":
         achieved = pbytes / (partial_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
     else:
         achieved = pflops / (partial_us * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None)
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic)
     roof.update(kernel="verify_partial_kernel", kernel_us=round(partial_us, 3), bytes_per_launch=pbytes,
                 flops_per_launch=pflops)
     gpu_out = out.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -432,7 +472,7 @@ def main():
 
     if not args.no_sweep:
         sweep = []
-        for ctx, t in [(65_536, 9), (65_536, 16), (131_072, 9), (184_728, 9), (184_728, 16), (65_536, 32)]:
+        for ctx, t in (FULL_SWEEP if args.full_sweep else SWEEP):
             sweep.append(sweep_point(torch, mv, ctx, t))
             log(f"sweep context {ctx} nodes {t}: {sweep[-1]['latency_us']} us, {sweep[-1]['eff_kv_gbs']} GB/s")
         line["sweep"] = sweep
