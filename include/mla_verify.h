@@ -86,7 +86,10 @@ typedef struct {
   int32_t head_dim_v;    /* must be 512: V is kv_cache[slot, 0:512] */
   int32_t page_size;     /* power of two >= 1 (1 for scattered tree slots, 64 for block pages) */
   int32_t max_pages;     /* row stride of page_table; a request holds <= max_pages*page_size keys */
-  int32_t nsplit;        /* >= 1 KV chunks per request; results do not depend on it beyond rounding */
+  int32_t nsplit;        /* >= 1: KV chunks per request on average. The B*nsplit chunk slots are
+                            shared out over the requests in proportion to their key counts
+                            (one at least each; equal lengths give nsplit each). Results do not
+                            depend on it beyond rounding. */
   int64_t num_kv_slots;  /* rows in kv_cache; slots >= this are out of range */
   int64_t kv_row_stride; /* elements between consecutive kv_cache rows: >= 576, multiple of 8 */
   float sm_scale;        /* softmax scale applied to q.k (1/sqrt(192) for 128 nope + 64 rope) */

@@ -150,6 +150,71 @@ __device__ __forceinline__ float xor32(float v) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Keys of request b after the clamp to [T, capacity] (the device-side guard
+// for seq_lens).
+__device__ __forceinline__ int clamped_len(const VerifyLaunch& L, int b) {
+  return min(max(L.seq_lens[b], L.nodes), L.capacity);
+}
+
+// Wave-wide inclusive prefix sum of v (64 lanes).
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t lo = __shfl_up(static_cast<uint32_t>(v), d);
+    const uint32_t hi = __shfl_up(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32), d);
+    const int64_t o = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Split plan: the grid's B*NSPLIT split slots are shared out over the
+// requests in proportion to their key counts, one slot at least each:
+// request b owns nsplit_b = 1 + floor((B*NSPLIT - B) * n_b / sum n) consecutive
+// slots from first_b = sum_{b' < b} nsplit_b'. Equal lengths give every request
+// NSPLIT slots at b*NSPLIT (the plain split of the method); ragged batches get
+// chunks of about the same size, so no request's keys set the step alone.
+// Slots past the last owned one stay idle. Computed by every wave from
+// seq_lens alone (no host data), identically in both kernels.
+struct SplitRange {
+  int b;      // owning request, -1 for an idle slot
+  int first;  // first slot of the request
+  int count;  // slots of the request
+};
+// by_slot: find the owner of slot `key`; otherwise the range of request `key`.
+__device__ SplitRange split_plan(const VerifyLaunch& L, int key, bool by_slot, int lane) {
+  const int B = L.batch;
+  if (B == 1) return SplitRange{by_slot ? (key < L.nsplit ? 0 : -1) : 0, 0, L.nsplit};
+  int64_t total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int i = base + lane;
+    const int64_t n = i < B ? clamped_len(L, i) : 0;
+    const int64_t sum = wave_incl_scan(n, lane);
+    total += static_cast<int64_t>(__shfl(static_cast<uint32_t>(sum), 63)) |
+             (static_cast<int64_t>(__shfl(static_cast<uint32_t>(static_cast<uint64_t>(sum) >> 32), 63)) << 32);
+  }
+  const int64_t spare = static_cast<int64_t>(B) * L.nsplit - B;
+  int64_t run = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int i = base + lane;
+    const int64_t n = i < B ? clamped_len(L, i) : 0;
+    const int64_t ns = i < B ? 1 + (total > 0 ? (spare * n) / total : 0) : 0;
+    const int64_t incl = wave_incl_scan(ns, lane);
+    const int64_t excl = incl - ns;
+    const bool own = i < B && (by_slot ? (key >= run + excl && key < run + incl) : i == key);
+    const uint64_t m = __ballot(own);
+    if (m != 0) {
+      const int src = __builtin_ctzll(m);
+      return SplitRange{base + src,
+                        __builtin_amdgcn_readfirstlane(static_cast<int>(run) + __shfl(static_cast<int>(excl), src)),
+                        __builtin_amdgcn_readfirstlane(__shfl(static_cast<int>(ns), src))};
+    }
+    run += static_cast<int64_t>(__shfl(static_cast<uint32_t>(incl), 63)) |
+           (static_cast<int64_t>(__shfl(static_cast<uint32_t>(static_cast<uint64_t>(incl) >> 32), 63)) << 32);
+  }
+  return SplitRange{-1, 0, 0};
+}
+
 // Ancestor-or-self bitmask of node `lane` (lanes >= T get 0) by pointer
 // jumping: after round r a node's mask covers ancestors closer than 2^r and its
 // pointer names the ancestor 2^r up. Six rounds cover 64 nodes. The whole wave
@@ -220,22 +285,25 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (logical >= total) return;
   const int rb = logical % L.row_blocks;
-  const int bs = logical / L.row_blocks;
-  const int s = bs % L.nsplit;
-  const int b = bs / L.nsplit;
+  const int slot = logical / L.row_blocks;  // split slot in [0, B*NSPLIT)
+  const SplitRange sr = split_plan(L, slot, true, lane);
+  if (sr.b < 0) return;  // idle slot: no request owns it and the combine never reads it
+  const int b = __builtin_amdgcn_readfirstlane(sr.b);
+  const int s = slot - __builtin_amdgcn_readfirstlane(sr.first);
+  const int nsplit_b = __builtin_amdgcn_readfirstlane(sr.count);
 
   const int T = L.nodes;
   const int n_raw = L.seq_lens[b];
   const int n = min(max(n_raw, T), L.capacity);
   if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
   const int ctx = n - T;
-  const int chunk = (n + L.nsplit - 1) / L.nsplit;
+  const int chunk = (n + nsplit_b - 1) / nsplit_b;
   const int k0 = s * chunk;
   const int k1 = min(n, k0 + chunk);
 
   const int row = rb * (NW * 32) + wid * 32 + (lane & 31);
   const bool row_ok = row < L.rows;
-  float* lse_dst = L.part_lse + (static_cast<size_t>(b) * L.nsplit + s) * L.rows_pad + row;
+  float* lse_dst = L.part_lse + static_cast<size_t>(slot) * L.rows_pad + row;
   if (k0 >= k1) {  // empty split: contributes nothing
     if (lane < 32) *lse_dst = -INFINITY;
     return;
@@ -634,7 +702,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   if (!row_ok) return;  // padding rows are never read
   const float inv = l_pb_t > 0.f ? 1.f / l_pb_t : 0.f;
   f32x4* dst = reinterpret_cast<f32x4*>(L.part_o) +
-               ((static_cast<size_t>(b) * L.nsplit + s) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
+               (static_cast<size_t>(slot) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
 #pragma unroll
   for (int cb = 0; cb < kColBlocks; ++cb)
 #pragma unroll
@@ -668,14 +736,15 @@ __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(Veri
   const int row = wb * 32 + (lane & 31);  // < rows_pad: its partial lse is always written
   const bool row_ok = row < L.rows;       // partial outputs exist for real rows only
 
-  const float* pl = L.part_lse + static_cast<size_t>(b) * L.nsplit * L.rows_pad + row;
+  const SplitRange sr = split_plan(L, b, false, lane);  // this request's split slots
+  const float* pl = L.part_lse + static_cast<size_t>(sr.first) * L.rows_pad + row;
   const size_t split_stride = static_cast<size_t>(nwb) * 4096;
-  const f32x4* po = reinterpret_cast<const f32x4*>(L.part_o) + static_cast<size_t>(b) * L.nsplit * split_stride +
+  const f32x4* po = reinterpret_cast<const f32x4*>(L.part_o) + static_cast<size_t>(sr.first) * split_stride +
                     static_cast<size_t>(wb) * 4096 + frag * 64 + lane;
   float mx = -INFINITY, wsum = 0.f;
   f32x4 acc = {};
 #pragma unroll 16
-  for (int s = w; s < L.nsplit; s += kCombineWaves) {
+  for (int s = w; s < sr.count; s += kCombineWaves) {
     const float l2 = pl[static_cast<size_t>(s) * L.rows_pad];
     const bool live = row_ok && l2 > -INFINITY;
     const f32x4 v = row_ok ? po[s * split_stride] : f32x4{};

@@ -94,6 +94,20 @@ def test_parity_small(spec):
     check_parity(case, out, lse, label=str(spec))
 
 
+@pytest.mark.parametrize("nsplit", [1, 3, 8, 64])
+def test_skewed_batch_split_plan(nsplit):
+    """One long request beside short ones: the split slots follow the key
+    counts (the short requests keep one slot at least) and every request's
+    result still matches the oracle."""
+    spec = dict(seed=211, batch=5, nodes=6, heads=8, contexts=[9000, 3, 40, 2100, 700], page_size=4,
+                tree="uniform", nsplit=nsplit)
+    case = small_case(**spec)
+    say(f"skewed batch {spec}")
+    out, lse, err = run_gpu(case)
+    assert err == 0
+    check_parity(case, out, lse, label=f"skewed nsplit={nsplit}")
+
+
 # ------------------------------------------------------------------ the named workloads
 
 @pytest.mark.parametrize("nsplit", [1, 4, 64])

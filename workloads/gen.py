@@ -174,7 +174,7 @@ def _c4(seed=4, nsplit=128, contiguous=False):
                              POOL_SLOTS_PAGES, tree, nsplit, contiguous=contiguous)
 
 
-def _c5(seed=5, nsplit=64, batch=8, t=12, heads=8, ps=64, lo=1024, hi=131_072):
+def _c5(seed=5, nsplit=32, batch=8, t=12, heads=8, ps=64, lo=1024, hi=131_072):
     rng = np.random.default_rng(seed)
     ctx = np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=batch))).astype(np.int64)
     n = ctx + t
