@@ -99,7 +99,7 @@ mla_status prepare(const mla_verify_desc* d, const void* q, const void* kv_cache
   L->lse = lse;
   L->err = reinterpret_cast<uint32_t*>(ws);
   L->part_lse = reinterpret_cast<float*>(ws + mlav::part_lse_offset());
-  L->part_o = reinterpret_cast<float*>(ws + mlav::part_o_offset(d->batch, d->nsplit, rp.rows_pad));
+  L->part_o = reinterpret_cast<uint16_t*>(ws + mlav::part_o_offset(d->batch, d->nsplit, rp.rows_pad));
   L->kv_row_bytes = d->kv_row_stride * 2;
   L->num_slots = d->num_kv_slots;
   L->batch = d->batch;

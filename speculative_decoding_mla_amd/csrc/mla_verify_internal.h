@@ -22,8 +22,8 @@ struct VerifyLaunch {
   uint16_t* out;               // bf16 [B, T, H, 512]
   float* lse;                  // [B, T, H]
   uint32_t* err;               // device error word (workspace head)
-  float* part_lse;             // [B, nsplit, rows_pad] log2-domain partial lse
-  float* part_o;               // fragment-ordered partial outputs (fp32)
+  float* part_lse;             // [B*nsplit slots][rows_pad] pairs {partial lse (log2 units), scale exponent}
+  uint16_t* part_o;            // fragment-ordered partial outputs, fp16, scaled by 2^-exponent
   int64_t kv_row_bytes;        // bytes between kv rows
   int64_t num_slots;
   int32_t batch, nodes, heads, rows, rows_pad, waves_per_wg, row_blocks;

@@ -66,6 +66,8 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -303,9 +305,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 
   const int row = rb * (NW * 32) + wid * 32 + (lane & 31);
   const bool row_ok = row < L.rows;
-  float* lse_dst = L.part_lse + static_cast<size_t>(slot) * L.rows_pad + row;
+  f32x2* lse_dst = reinterpret_cast<f32x2*>(L.part_lse) + static_cast<size_t>(slot) * L.rows_pad + row;
   if (k0 >= k1) {  // empty split: contributes nothing
-    if (lane < 32) *lse_dst = -INFINITY;
+    if (lane < 32) *lse_dst = f32x2{-INFINITY, 0.f};
     return;
   }
 
@@ -693,23 +695,35 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     run_pass(PassMode<kPassFixed>{});
   }
 
-  // ---- partial result of this split: O / l (fp32) and lse in log2 units
+  // ---- partial result of this split: O / l in fp16 and lse in log2 units.
+  // O / l is a convex combination of V rows; it is stored as fp16 scaled by
+  // 2^-e, with e = 0 unless the row's largest |O / l| reaches 2^15 (then the
+  // smallest e that brings it below), and e is kept beside the lse. fp16 adds
+  // at most 2^-12 relative to each stored value, well inside one bf16 rounding
+  // of the final output.
   // (wait states between the last XDL write of O and the reads below)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
   const float l_sum_t = l_sum + __shfl_xor(l_sum, 32);
   const float l_pb_t = l_pb + __shfl_xor(l_pb, 32);
-  if (lane < 32) *lse_dst = l_sum_t > 0.f ? m_ref + __builtin_amdgcn_logf(l_sum_t) : -INFINITY;
-  if (!row_ok) return;  // padding rows are never read
   const float inv = l_pb_t > 0.f ? 1.f / l_pb_t : 0.f;
-  f32x4* dst = reinterpret_cast<f32x4*>(L.part_o) +
-               (static_cast<size_t>(slot) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
+  float amax = 0.f;
 #pragma unroll
   for (int cb = 0; cb < kColBlocks; ++cb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-    {
-      dst[(cb * 4 + q) * 64] = f32x4{o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv,
-                                     o[cb][4 * q + 3] * inv};
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(o[cb][j]));
+  amax = fmaxf(amax, xor32(amax)) * inv;  // the row's 512 values sit on lanes l and l ^ 32
+  const int e = max(0, __builtin_amdgcn_frexp_expf(amax) - 15);
+  if (lane < 32)
+    *lse_dst = f32x2{l_sum_t > 0.f ? m_ref + __builtin_amdgcn_logf(l_sum_t) : -INFINITY, static_cast<float>(e)};
+  if (!row_ok) return;  // padding rows are never read
+  const float sc = __builtin_ldexpf(inv, -e);
+  f16x4* dst = reinterpret_cast<f16x4*>(L.part_o) + (static_cast<size_t>(slot) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
+#pragma unroll
+  for (int cb = 0; cb < kColBlocks; ++cb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = f32x4{o[cb][4 * q], o[cb][4 * q + 1], o[cb][4 * q + 2], o[cb][4 * q + 3]} * sc;
+      dst[(cb * 4 + q) * 64] = __builtin_convertvector(v, f16x4);
       if (q == 3) __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -718,11 +732,12 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 // kCombineWaves waves of the workgroup take every kCombineWaves-th split and
 // keep a running merge per lane (its row, four columns): M = largest lse so
 // far, acc = sum 2^(lse_s - M) O_s, w = sum 2^(lse_s - M), rescaled when M
-// grows; empty splits (lse = -inf) are skipped. The waves' states are merged
-// the same way in LDS. out = acc / w rounded to bf16 once; lse = M + log2 w in
-// natural-log units.
-constexpr int kCombineWaves = 8;
-
+// grows (O_s = stored fp16 x 2^e_s); empty splits (lse = -inf) are skipped. The
+// waves' states are merged the same way in LDS. out = acc / w rounded to bf16
+// once; lse = M + log2 w in natural-log units.
+// A small grid (one request: a few 32-row blocks x 64 fragment slots) takes
+// 16 waves per workgroup to keep enough loads in flight; a large one 8.
+template <int kCombineWaves>
 __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(VerifyLaunch L) {
   __shared__ f32x4 red_acc[kCombineWaves][64];
   __shared__ float red_w[kCombineWaves][64];
@@ -737,21 +752,24 @@ __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(Veri
   const bool row_ok = row < L.rows;       // partial outputs exist for real rows only
 
   const SplitRange sr = split_plan(L, b, false, lane);  // this request's split slots
-  const float* pl = L.part_lse + static_cast<size_t>(sr.first) * L.rows_pad + row;
+  const int first = __builtin_amdgcn_readfirstlane(sr.first);
+  const int count = __builtin_amdgcn_readfirstlane(sr.count);
+  const f32x2* pl = reinterpret_cast<const f32x2*>(L.part_lse) + static_cast<size_t>(first) * L.rows_pad + row;
   const size_t split_stride = static_cast<size_t>(nwb) * 4096;
-  const f32x4* po = reinterpret_cast<const f32x4*>(L.part_o) + static_cast<size_t>(sr.first) * split_stride +
+  const f16x4* po = reinterpret_cast<const f16x4*>(L.part_o) + static_cast<size_t>(first) * split_stride +
                     static_cast<size_t>(wb) * 4096 + frag * 64 + lane;
   float mx = -INFINITY, wsum = 0.f;
   f32x4 acc = {};
 #pragma unroll 16
-  for (int s = w; s < sr.count; s += kCombineWaves) {
-    const float l2 = pl[static_cast<size_t>(s) * L.rows_pad];
+  for (int s = w; s < count; s += kCombineWaves) {
+    const f32x2 le = pl[static_cast<size_t>(s) * L.rows_pad];
+    const float l2 = le[0];
     const bool live = row_ok && l2 > -INFINITY;
-    const f32x4 v = row_ok ? po[s * split_stride] : f32x4{};
+    const f32x4 v = row_ok ? __builtin_convertvector(po[s * split_stride], f32x4) : f32x4{};
     const float nm = live ? fmaxf(mx, l2) : mx;
     const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - nm);
     const float wt = live ? __builtin_amdgcn_exp2f(l2 - nm) : 0.f;
-    acc = acc * sc + wt * (live ? v : f32x4{});
+    acc = acc * sc + __builtin_ldexpf(wt, static_cast<int>(le[1])) * (live ? v : f32x4{});
     wsum = wsum * sc + wt;
     mx = nm;
   }
@@ -777,11 +795,9 @@ __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(Veri
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const f32x4 r = acc * inv;
   const int col = (frag >> 2) * 32 + (frag & 3) * 8 + (lane >> 5) * 4;
-  const bf16x2 lo = __builtin_convertvector(f32x2{r[0], r[1]}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector(f32x2{r[2], r[3]}, bf16x2);
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4* dst = reinterpret_cast<bf16x4*>(L.out + (static_cast<size_t>(b) * L.rows + row) * kVDim + col);
-  *dst = bf16x4{lo[0], lo[1], hi[0], hi[1]};
+  *reinterpret_cast<bf16x4*>(L.out + (static_cast<size_t>(b) * L.rows + row) * kVDim + col) =
+      __builtin_convertvector(r, bf16x4);
   if (frag == 0 && lane < 32)
     L.lse[static_cast<size_t>(b) * L.rows + row] =
         wsum > 0.f ? (m_all + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f : -INFINITY;
@@ -802,13 +818,13 @@ RowPlan plan_rows(int nodes, int heads) {
 size_t part_lse_offset() { return kHeaderBytes; }
 
 size_t part_o_offset(int batch, int nsplit, int rows_pad) {
-  const size_t lse_bytes = static_cast<size_t>(batch) * nsplit * rows_pad * sizeof(float);
+  const size_t lse_bytes = static_cast<size_t>(batch) * nsplit * rows_pad * 2 * sizeof(float);
   return (part_lse_offset() + lse_bytes + 255) & ~static_cast<size_t>(255);
 }
 
 size_t workspace_bytes(int batch, int nsplit, int rows_pad) {
   return part_o_offset(batch, nsplit, rows_pad) +
-         static_cast<size_t>(batch) * nsplit * rows_pad * kVDim * sizeof(float);
+         static_cast<size_t>(batch) * nsplit * rows_pad * kVDim * sizeof(uint16_t);
 }
 
 hipError_t launch_tree_mask(const int32_t* tree_parent, uint64_t* anc, int batch, int nodes,
@@ -831,7 +847,10 @@ hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream) {
 
 hipError_t launch_combine(const VerifyLaunch& L, hipStream_t stream) {
   const int cgrid = L.batch * (L.rows_pad / 32) * 64;
-  hipLaunchKernelGGL(verify_combine_kernel, dim3(cgrid), dim3(kCombineWaves * 64), 0, stream, L);
+  if (cgrid <= 512)
+    hipLaunchKernelGGL(verify_combine_kernel<16>, dim3(cgrid), dim3(16 * 64), 0, stream, L);
+  else
+    hipLaunchKernelGGL(verify_combine_kernel<8>, dim3(cgrid), dim3(8 * 64), 0, stream, L);
   return hipGetLastError();
 }
 
