@@ -1,4 +1,7 @@
-"""CPU oracle for tree-masked MLA verify attention over a paged latent KV pool.
+"""CPU oracles for tree-masked MLA verify attention over a paged latent KV pool
+(mla_oracle) and for the steps next to it (spec_ops_oracle: sparse top-k
+decode, tree accept, KV append and commit, sliding-window gather, fp8 indexer
+logits).
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import or run anything in this package. The
