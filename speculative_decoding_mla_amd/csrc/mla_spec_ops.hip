@@ -1,0 +1,359 @@
+// gfx950 (MI355X) kernels for the steps next to the verify attention: the
+// draft rows' KV append, the greedy tree accept, the commit (and optional
+// relocation) of the accepted path, the page-aligned sliding-window map of a
+// draft cache, and the DSA indexer logits over an fp8 paged cache.
+//
+// The first four are integer and byte work: each is laid out for coalesced
+// 16-byte (rows) or 4-byte (maps) accesses, with the per-request logic of a
+// draft tree (at most 64 nodes) done inside one wave by pointer jumping. The
+// indexer is a small dense contraction per cache block (64 positions x 64
+// heads x 128 dims): its fp8 operands are widened exactly to bf16 and fed to
+// v_mfma_f32_32x32x16_bf16 straight from global memory, and the ReLU /
+// weight / head-sum / scale epilogue runs through LDS. Every grid is fixed by
+// host-known sizes; blocks past a request's length exit after writing -inf.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_spec_ops.h"
+#include "mla_spec_ops_internal.h"
+
+namespace mlav {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowChunks = 72;  // 16-byte chunks of a 1,152-byte latent row
+
+__device__ __forceinline__ void flag(uint32_t* err, uint32_t bit) {
+  if (err != nullptr) atomicOr(err, bit);
+}
+
+// ---------------------------------------------------------------- KV append
+
+__global__ __launch_bounds__(256) void kv_append_kernel(uint8_t* __restrict__ kv, int64_t num_slots,
+                                                        int64_t row_bytes, const uint8_t* __restrict__ rows,
+                                                        const int32_t* __restrict__ loc, int n, uint32_t* err) {
+  const int64_t total = static_cast<int64_t>(n) * kRowChunks;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = t / kRowChunks;
+    const int c = static_cast<int>(t - r * kRowChunks);
+    const int32_t slot = loc[r];
+    if (slot < 0 || slot >= num_slots) {
+      if (c == 0) flag(err, MLA_DEVERR_SLOT_RANGE);
+      continue;
+    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(rows + r * (kRowChunks * 16) + c * 16);
+    *reinterpret_cast<u32x4*>(kv + slot * row_bytes + c * 16) = v;
+  }
+}
+
+// ---------------------------------------------------------------- tree helpers (one wave, lane = node)
+
+// Parent of node `lane` (-1 for lanes >= T); a parent outside [-1, lane) is
+// reported and read as -1 (a root).
+__device__ __forceinline__ int checked_parent(const int32_t* parents, int T, int lane, uint32_t* err) {
+  int p = lane < T ? parents[lane] : -1;
+  const bool bad = lane < T && (p < -1 || p >= lane);
+  if (bad) p = -1;
+  if (__any(bad) && lane == 0) flag(err, MLA_DEVERR_BAD_PARENT);
+  return p;
+}
+
+// Pointer jumping over parent links (six rounds cover 64 nodes): `all` becomes
+// the AND of `f` over the node and its ancestors, `anc` the ancestor-or-self
+// bitmask and `depth` the number of links to the root.
+__device__ __forceinline__ void climb(int parent, bool f, int lane, int T, bool& all, uint64_t& anc, int& depth) {
+  int p = parent;
+  all = lane < T && f;
+  anc = lane < T ? 1ull << lane : 0ull;
+  depth = p >= 0 ? 1 : 0;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = p >= 0 ? p : lane;
+    const bool all_p = __shfl(static_cast<int>(all), src) != 0;
+    const uint32_t lo = __shfl(static_cast<uint32_t>(anc), src);
+    const uint32_t hi = __shfl(static_cast<uint32_t>(anc >> 32), src);
+    const int depth_p = __shfl(depth, src);
+    const int p2 = __shfl(p, src);
+    if (p >= 0) {
+      all = all && all_p;
+      anc |= (static_cast<uint64_t>(hi) << 32) | lo;
+      depth += depth_p;
+      p = p2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- greedy tree accept (one wave per request)
+
+__global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restrict__ parents,
+                                                         const int32_t* __restrict__ draft,
+                                                         const int32_t* __restrict__ target, int T,
+                                                         int32_t* __restrict__ accept_len,
+                                                         int32_t* __restrict__ path, int32_t* __restrict__ commit,
+                                                         uint32_t* err) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const size_t base = static_cast<size_t>(b) * T;
+  const int p = checked_parent(parents + base, T, lane, err);
+  const int d = lane < T ? draft[base + lane] : 0;
+  const int tg = lane < T ? target[base + lane] : 0;
+  // a root is accepted; another node iff its draft equals the target's choice after its parent
+  const int tg_parent = __shfl(tg, p >= 0 ? p : lane);
+  const bool match = p < 0 || d == tg_parent;
+  bool acc;
+  uint64_t anc;
+  int depth;
+  climb(p, match, lane, T, acc, anc, depth);
+  // deepest accepted node, the smaller index among equals: max of depth * 64 + (63 - lane)
+  int key = acc ? depth * 64 + (63 - lane) : -1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) key = max(key, __shfl_xor(key, o));
+  const int best = 63 - (key & 63);  // node 0 is a root (parent -1), so key >= 0
+  const int best_depth = key >> 6;
+  const uint32_t blo = __shfl(static_cast<uint32_t>(anc), best);
+  const uint32_t bhi = __shfl(static_cast<uint32_t>(anc >> 32), best);
+  const uint64_t on_path = (static_cast<uint64_t>(bhi) << 32) | blo;
+  const int n_acc = best_depth + 1;
+  if (lane == 0) accept_len[b] = n_acc;
+  if (lane < T) {
+    const bool mine = (on_path >> lane) & 1ull;
+    const int pos = __popcll(on_path & ((1ull << lane) - 1ull));  // place on the path (root = 0)
+    if (mine) path[base + pos] = lane;
+    if (lane >= n_acc) path[base + lane] = -1;
+    if (commit != nullptr) {
+      if (mine && pos >= 1) commit[base + pos - 1] = d;
+      if (lane == best) commit[base + best_depth] = tg;
+      if (lane > best_depth) commit[base + lane] = -1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- commit of the accepted path (one workgroup per request)
+
+constexpr int kCommitThreads = 256;
+
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitLaunch C) {
+  __shared__ int32_t tree_slot[kMaxTreeNodes];
+  __shared__ int32_t path_s[kMaxTreeNodes];
+  __shared__ int32_t n_acc_s, c0_s;
+  __shared__ uint64_t on_path_s;
+  __shared__ __attribute__((aligned(16))) uint8_t rows_s[kMaxTreeNodes * kRowChunks * 16];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int T = C.nodes;
+  const size_t tb = static_cast<size_t>(b) * T;
+  if (tid == 0) {
+    const int sl = C.seq_lens[b];
+    const int sl_c = min(max(sl, T), C.max_pages);
+    const int na = C.accept_len[b];
+    const int na_c = min(max(na, 1), T);
+    if (sl != sl_c || na != na_c) flag(C.err, MLA_DEVERR_INDEX_RANGE);
+    c0_s = sl_c - T;
+    n_acc_s = na_c;
+    on_path_s = 0ull;
+  }
+  __syncthreads();
+  const int c0 = c0_s, n_acc = n_acc_s;
+  int32_t* row = C.page_table + static_cast<size_t>(b) * C.max_pages;
+  if (tid < T) {
+    tree_slot[tid] = row[c0 + tid];
+    if (tid < n_acc) {
+      int j = C.path[tb + tid];
+      if (j < 0 || j >= T) {
+        flag(C.err, MLA_DEVERR_INDEX_RANGE);
+        j = min(max(j, 0), T - 1);
+      }
+      path_s[tid] = j;
+      atomicOr(reinterpret_cast<unsigned long long*>(&on_path_s), 1ull << j);
+    }
+  }
+  __syncthreads();
+  // relocation: every accepted row is read into LDS before any is written
+  if (C.dest != nullptr) {
+    for (int t = tid; t < n_acc * kRowChunks; t += kCommitThreads) {
+      const int k = t / kRowChunks, c = t - k * kRowChunks;
+      const int32_t src = tree_slot[path_s[k]];
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (src >= 0 && src < C.num_slots) v = *reinterpret_cast<const u32x4*>(C.kv + src * C.row_bytes + c * 16);
+      *reinterpret_cast<u32x4*>(rows_s + t * 16) = v;
+    }
+    __syncthreads();
+    for (int t = tid; t < n_acc * kRowChunks; t += kCommitThreads) {
+      const int k = t / kRowChunks, c = t - k * kRowChunks;
+      const int32_t src = tree_slot[path_s[k]];
+      const int32_t dst = C.dest[tb + k];
+      const bool ok = src >= 0 && src < C.num_slots && dst >= 0 && dst < C.num_slots;
+      if (!ok) {
+        if (c == 0) flag(C.err, MLA_DEVERR_SLOT_RANGE);
+        continue;
+      }
+      *reinterpret_cast<u32x4*>(C.kv + dst * C.row_bytes + c * 16) = *reinterpret_cast<const u32x4*>(rows_s + t * 16);
+    }
+  }
+  if (tid < n_acc) row[c0 + tid] = C.dest != nullptr ? C.dest[tb + tid] : tree_slot[path_s[tid]];
+  if (tid < T && C.freed != nullptr) {
+    const uint64_t on_path = on_path_s;
+    const bool kept = (on_path >> tid) & 1ull;
+    const uint64_t below = (tid == 0 ? 0ull : (~0ull >> (64 - tid)));
+    const int pos = tid - __popcll(on_path & below);  // released nodes before this one
+    if (!kept) C.freed[tb + pos] = tree_slot[tid];
+    if (tid >= T - n_acc) C.freed[tb + tid] = -1;
+  }
+  if (tid == 0) C.context_lens[b] = c0 + n_acc;
+}
+
+// ---------------------------------------------------------------- sliding-window map
+
+__global__ __launch_bounds__(256) void window_map_kernel(const int32_t* __restrict__ target_map, int map_stride,
+                                                         const int32_t* __restrict__ lens, int W, int P,
+                                                         int32_t* __restrict__ draft_map,
+                                                         int32_t* __restrict__ compact_lens, uint32_t* err) {
+  const int b = blockIdx.y;
+  const int width = W + P - 1;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int raw = lens[b];
+  const int L = min(max(raw, 0), map_stride);
+  const int start = ((L - min(L, W)) / P) * P;  // page-aligned window start s(L)
+  const int c = L - start;                       // compact length c(L)
+  if (j == 0) {
+    if (raw != L) flag(err, MLA_DEVERR_SEQ_LEN);
+    if (compact_lens != nullptr) compact_lens[b] = c;
+  }
+  if (j < width)
+    draft_map[static_cast<size_t>(b) * width + j] =
+        j < c ? target_map[static_cast<size_t>(b) * map_stride + start + j] : -1;
+}
+
+// ---------------------------------------------------------------- fp8 indexer logits
+
+// Eight E4M3 codes (two dwords) widened exactly to bf16: the hardware
+// conversion gives fp32, and a value with at most four significant bits is a
+// bf16 whose pattern is the fp32 pattern's upper half.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v packed = {
+      (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u),
+      (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u),
+      (__float_as_uint(c[0]) >> 16) | (__float_as_uint(c[1]) & 0xffff0000u),
+      (__float_as_uint(d[0]) >> 16) | (__float_as_uint(d[1]) & 0xffff0000u)};
+  return __builtin_bit_cast(bf16x8, packed);
+}
+
+constexpr int kIdxPage = 64, kIdxDim = 128, kIdxBlockBytes = 8448, kIdxScaleOff = kIdxPage * kIdxDim;
+
+// One workgroup of four waves per (request, block). Wave w computes the
+// 32 x 32 tile (positions 32 (w & 1) + 0..31) x (heads 32 (w >> 1) + 0..31) of
+// K Q^T with eight MFMAs. The contraction index is permuted the same way on
+// both sides: k-step ks and lane half hs cover dims 64 hs + 8 ks + 0..7, so
+// each lane's operand bytes for all eight steps are 64 contiguous bytes of its
+// position's row (A) and its head's row (B).
+__global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
+  __shared__ float red[4][32][33];  // [wave][position][head], padded against bank conflicts
+  const int b = blockIdx.y;
+  const int page = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hs = lane >> 5;
+  const int raw = I.seq_lens[b];
+  const int cap = I.max_blocks * kIdxPage;
+  const int n = min(max(raw, 0), cap);
+  if (raw != n && page == 0 && tid == 0) flag(I.err, MLA_DEVERR_SEQ_LEN);
+  float* out = I.logits + static_cast<size_t>(b) * cap + static_cast<size_t>(page) * kIdxPage;
+  const int pos0 = page * kIdxPage;
+  if (pos0 >= n) {  // past the request's length: nothing to read
+    if (tid < kIdxPage) out[tid] = -INFINITY;
+    return;
+  }
+  const int32_t blk = I.block_table[static_cast<size_t>(b) * I.max_blocks + page];
+  if (blk < 0 || blk >= I.num_blocks) {
+    if (tid == 0) flag(I.err, MLA_DEVERR_SLOT_RANGE);
+    if (tid < kIdxPage) out[tid] = -INFINITY;
+    return;
+  }
+  const uint8_t* block = I.kv_blocks + static_cast<size_t>(blk) * kIdxBlockBytes;
+  const int pb = w & 1, hb = w >> 1;
+  const int pos = pb * 32 + (lane & 31);
+  const int head = hb * 32 + (lane & 31);
+  const bool head_ok = head < I.heads;
+  const u32x4* arow = reinterpret_cast<const u32x4*>(block + pos * kIdxDim + hs * 64);
+  const u32x4* brow = reinterpret_cast<const u32x4*>(I.q + (static_cast<size_t>(b) * I.heads + (head_ok ? head : 0)) * kIdxDim + hs * 64);
+  u32x4 av[4], bv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    av[i] = arow[i];
+    bv[i] = head_ok ? brow[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4& a = av[ks >> 1];
+    const u32x4& q = bv[ks >> 1];
+    const int o = (ks & 1) * 2;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(a[o], a[o + 1]), e4m3x8_to_bf16(q[o], q[o + 1]),
+                                                   acc, 0, 0, 0);
+  }
+  // lane holds C[r][lane % 32] for r = 8 (j / 4) + 4 hs + j % 4: ReLU, head weight
+  const float wt = head_ok ? I.weights[static_cast<size_t>(b) * I.heads + head] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) red[w][8 * (j >> 2) + 4 * hs + (j & 3)][lane & 31] = wt * fmaxf(acc[j], 0.f);
+  __syncthreads();
+  if (tid < kIdxPage) {
+    const int p = tid;  // position in the block
+    const int pbl = p >> 5, r = p & 31;
+    float s = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) s += red[pbl][r][c] + red[pbl + 2][r][c];
+    const float scale = reinterpret_cast<const float*>(block + kIdxScaleOff)[p];
+    out[p] = pos0 + p < n ? s * scale : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(uint8_t* kv, int64_t num_slots, int64_t row_bytes, const uint8_t* rows,
+                            const int32_t* loc, int n, uint32_t* err, hipStream_t stream) {
+  const int64_t chunks = static_cast<int64_t>(n) * kRowChunks;
+  const int64_t want = (chunks + 255) / 256;
+  const int grid = static_cast<int>(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(256), 0, stream, kv, num_slots, row_bytes, rows, loc, n, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target, int batch, int T,
+                              int32_t* accept_len, int32_t* path, int32_t* commit, uint32_t* err,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(batch), dim3(64), 0, stream, parents, draft, target, T, accept_len,
+                     path, commit, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitLaunch& C, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_kernel, dim3(C.batch), dim3(kCommitThreads), 0, stream, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_map(const int32_t* target_map, int map_stride, const int32_t* lens, int batch, int W,
+                             int P, int32_t* draft_map, int32_t* compact_lens, uint32_t* err, hipStream_t stream) {
+  const int width = W + P - 1;
+  hipLaunchKernelGGL(window_map_kernel, dim3((width + 255) / 256, batch), dim3(256), 0, stream, target_map,
+                     map_stride, lens, W, P, draft_map, compact_lens, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer(const IndexerLaunch& I, hipStream_t stream) {
+  hipLaunchKernelGGL(indexer_kernel, dim3(I.max_blocks, I.batch), dim3(256), 0, stream, I);
+  return hipGetLastError();
+}
+
+}  // namespace mlav

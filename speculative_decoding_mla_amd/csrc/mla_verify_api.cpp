@@ -113,6 +113,8 @@ mla_status prepare(const mla_verify_desc* d, const void* q, const void* kv_cache
   L->page_shift = log2i(d->page_size);
   L->max_pages = d->max_pages;
   L->capacity = static_cast<int32_t>(static_cast<int64_t>(d->max_pages) * d->page_size);
+  L->min_len = d->num_nodes;
+  L->quiet_unused = 0;
   L->scale_log2 = d->sm_scale * 1.4426950408889634f;
   return MLA_OK;
 }

@@ -17,8 +17,8 @@ struct VerifyLaunch {
   const uint16_t* q;           // bf16 [B, T, H, 576]
   const uint8_t* kv;           // bf16 rows, byte pointer
   const int32_t* page_table;   // [B, max_pages]
-  const int32_t* seq_lens;     // [B]
-  const int32_t* tree_parent;  // [B, T]
+  const int32_t* seq_lens;     // [B]; null: every request holds capacity keys
+  const int32_t* tree_parent;  // [B, T]; null: every node is a root
   uint16_t* out;               // bf16 [B, T, H, 512]
   float* lse;                  // [B, T, H]
   uint32_t* err;               // device error word (workspace head)
@@ -29,6 +29,8 @@ struct VerifyLaunch {
   int32_t batch, nodes, heads, rows, rows_pad, waves_per_wg, row_blocks;
   int32_t nsplit, page_shift, max_pages;
   int32_t capacity;            // max_pages * page_size (clamp bound for seq_lens)
+  int32_t min_len;             // lower clamp bound for seq_lens: T (verify) or 0 (sparse decode)
+  int32_t quiet_unused;        // 1: a page id of -1 is an unused entry, masked without an error bit
   float scale_log2;            // sm_scale * log2(e)
 };
 

@@ -152,10 +152,14 @@ __device__ __forceinline__ float xor32(float v) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// Keys of request b after the clamp to [T, capacity] (the device-side guard
-// for seq_lens).
+// Keys of request b as given (all of the table's capacity when no lengths
+// are passed), and after the clamp to [min_len, capacity] (the device-side
+// guard for seq_lens; min_len is T for verify, 0 for sparse decode).
+__device__ __forceinline__ int raw_len(const VerifyLaunch& L, int b) {
+  return L.seq_lens != nullptr ? L.seq_lens[b] : L.capacity;
+}
 __device__ __forceinline__ int clamped_len(const VerifyLaunch& L, int b) {
-  return min(max(L.seq_lens[b], L.nodes), L.capacity);
+  return min(max(raw_len(L, b), L.min_len), L.capacity);
 }
 
 // Wave-wide inclusive prefix sum of v (64 lanes).
@@ -295,8 +299,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int nsplit_b = __builtin_amdgcn_readfirstlane(sr.count);
 
   const int T = L.nodes;
-  const int n_raw = L.seq_lens[b];
-  const int n = min(max(n_raw, T), L.capacity);
+  const int n_raw = raw_len(L, b);
+  const int n = min(max(n_raw, L.min_len), L.capacity);
   if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
   const int ctx = n - T;
   const int chunk = (n + nsplit_b - 1) / nsplit_b;
@@ -533,13 +537,17 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
         slot_s[i] = ok ? static_cast<int32_t>(slot) : 0;
         if (!ok) {
           atomicOr(&badbits_s[i >> 5], 1u << (i & 31));
-          bad = 1;
+          // an unused entry (-1) of a sparse index list is masked quietly
+          if (!(L.quiet_unused && page == -1)) bad = 1;
         }
       }
       const int wave_bad = __any(bad);
       if (lane == 0) badw_s[wid] = wave_bad;
       if (kMode == kPassAdaptive && need_mask && w0 == k0 && wid == 0) {
-        const uint64_t a = ancestor_bits(L.tree_parent + static_cast<size_t>(b) * T, T, lane, L.err);
+        // without a parent array every node is a root (one query token per request)
+        const uint64_t a = L.tree_parent != nullptr
+                               ? ancestor_bits(L.tree_parent + static_cast<size_t>(b) * T, T, lane, L.err)
+                               : (lane < T ? 1ull << lane : 0ull);
         anc_s[lane] = a;
       }
       lds_barrier();

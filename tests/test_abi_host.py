@@ -13,12 +13,13 @@ from speculative_decoding_mla_amd import binding as bd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+HEADER_OPS = os.path.join(ROOT, "include", "mla_spec_ops.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="library not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_\w+)\s*\(", text)
 
 
@@ -27,8 +28,11 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"mla_verify_workspace_bytes", "mla_build_tree_mask", "mla_verify_attention",
                           "mla_verify_partial", "mla_verify_combine", "mla_status_string",
                           "mla_verify_abi_version"}
+    ops = declared_functions(HEADER_OPS)
+    assert set(ops) == {"mla_sparse_decode_workspace_bytes", "mla_sparse_decode", "mla_kv_append",
+                        "mla_tree_accept", "mla_commit_accepted", "mla_window_map", "mla_indexer_logits"}
     lib = ctypes.CDLL(bd.LIB_PATH)
-    for n in names:
+    for n in names + ops:
         assert hasattr(lib, n), n
 
 
@@ -124,3 +128,78 @@ def test_tree_mask_argument_checks():
     assert lib.mla_build_tree_mask(a, a, 0, 4, None, None) == -2
     assert lib.mla_build_tree_mask(a, a, 1, 0, None, None) == -2
     assert lib.mla_build_tree_mask(a, a, 1, 65, None, None) == -2
+
+
+# ---------------------------------------------------------------- the steps next to verify (mla_spec_ops.h)
+
+def _sdesc(**kw):
+    base = dict(batch=2, num_heads=64, head_dim_qk=576, head_dim_v=512, topk=512, nsplit=8, num_kv_slots=10_000,
+                kv_row_stride=576, sm_scale=0.07)
+    base.update(kw)
+    return bd.MlaSparseDesc(*[base[f] for f, _ in bd.MlaSparseDesc._fields_])
+
+
+def test_sparse_workspace_matches_verify_with_one_node():
+    # the sparse call is a verify call with one node: same workspace formula
+    d = _sdesc()
+    v = bd.make_desc(batch=2, num_nodes=1, num_heads=64, page_size=1, max_pages=512, nsplit=8, num_kv_slots=10_000)
+    lib = bd.load_library()
+    assert lib.mla_sparse_decode_workspace_bytes(ctypes.byref(d)) == bd.workspace_bytes(v) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -2), (dict(num_heads=0), -2), (dict(topk=0), -2), (dict(nsplit=0), -2),
+    (dict(num_kv_slots=0), -2), (dict(kv_row_stride=570), -2), (dict(head_dim_qk=512), -3), (dict(head_dim_v=576), -3),
+])
+def test_sparse_bad_descriptor_rejected(kw, status):
+    lib = bd.load_library()
+    d = _sdesc(**kw)
+    assert lib.mla_sparse_decode_workspace_bytes(ctypes.byref(d)) == 0
+    a = 1 << 20
+    assert lib.mla_sparse_decode(ctypes.byref(d), a, a, a, None, a, a, a, 1 << 40, None) == status
+
+
+def test_sparse_pointer_checks():
+    lib = bd.load_library()
+    d = _sdesc()
+    need = lib.mla_sparse_decode_workspace_bytes(ctypes.byref(d))
+    a = 1 << 20
+    assert lib.mla_sparse_decode(None, a, a, a, None, a, a, a, need, None) == -1
+    assert lib.mla_sparse_decode(ctypes.byref(d), None, a, a, None, a, a, a, need, None) == -1
+    assert lib.mla_sparse_decode(ctypes.byref(d), a, a, None, None, a, a, a, need, None) == -1
+    assert lib.mla_sparse_decode(ctypes.byref(d), a + 8, a, a, None, a, a, a, need, None) == -5
+    assert lib.mla_sparse_decode(ctypes.byref(d), a, a, a + 2, None, a, a, a, need, None) == -5
+    assert lib.mla_sparse_decode(ctypes.byref(d), a, a, a, None, a, a, a, need - 1, None) == -4
+
+
+def test_step_entry_points_check_arguments():
+    lib = bd.load_library()
+    a = 1 << 20
+    # kv append: n = 0 enqueues nothing and succeeds; bad shapes, nulls, alignment
+    assert lib.mla_kv_append(a, 100, 576, a, a, 0, None, None) == 0
+    assert lib.mla_kv_append(a, 100, 576, a, a, -1, None, None) == -2
+    assert lib.mla_kv_append(a, 100, 570, a, a, 1, None, None) == -2
+    assert lib.mla_kv_append(None, 100, 576, a, a, 1, None, None) == -1
+    assert lib.mla_kv_append(a + 4, 100, 576, a, a, 1, None, None) == -5
+    # tree accept
+    assert lib.mla_tree_accept(None, a, a, 1, 4, a, a, None, None, None) == -1
+    assert lib.mla_tree_accept(a, a, a, 1, 65, a, a, None, None, None) == -2
+    assert lib.mla_tree_accept(a, a, a, 0, 4, a, a, None, None, None) == -2
+    # commit: kv_cache and dest_slots go together; T <= max_pages
+    assert lib.mla_commit_accepted(a, 100, a, 1, 4, a, a, a, None, a, 10, 576, None, None, None) == -1
+    assert lib.mla_commit_accepted(a, 3, a, 1, 4, a, a, a, None, None, 0, 0, None, None, None) == -2
+    assert lib.mla_commit_accepted(a, 100, a, 1, 4, a, a, a, None, a + 8, 10, 576, a, None, None) == -5
+    # window map
+    assert lib.mla_window_map(a, 100, a, 1, 0, 64, a, None, None, None) == -2
+    assert lib.mla_window_map(None, 100, a, 1, 4096, 64, a, None, None, None) == -1
+    # indexer
+    desc = bd.MlaIndexerDesc(1, 64, 128, 10, 20)
+    assert lib.mla_indexer_logits(ctypes.byref(desc), a, a, a, a, a, None, None, None) == -1
+    desc = bd.MlaIndexerDesc(1, 65, 128, 10, 20)
+    assert lib.mla_indexer_logits(ctypes.byref(desc), a, a, a, a, a, a, None, None) == -3
+    desc = bd.MlaIndexerDesc(1, 64, 64, 10, 20)
+    assert lib.mla_indexer_logits(ctypes.byref(desc), a, a, a, a, a, a, None, None) == -3
+    desc = bd.MlaIndexerDesc(1, 64, 128, 0, 20)
+    assert lib.mla_indexer_logits(ctypes.byref(desc), a, a, a, a, a, a, None, None) == -2
+    desc = bd.MlaIndexerDesc(1, 64, 128, 10, 20)
+    assert lib.mla_indexer_logits(ctypes.byref(desc), a + 8, a, a, a, a, a, None, None) == -5
