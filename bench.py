@@ -328,6 +328,214 @@ def cpu_model():
     return "unknown"
 
 
+# ---------------------------------------------------------------- the steps next to verify
+
+def graph_us_per_call(torch, calls, reps=10):
+    """Per-call device time of `calls`, captured in one hipGraph and replayed
+    `reps` times between two events."""
+    g = capture(torch, calls)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+
+
+def _cpu_time(fn, budget_s=5.0, max_reps=5):
+    times, out = [], None
+    t_start = time.perf_counter()
+    while len(times) < max_reps:
+        t = time.perf_counter()
+        out = fn()
+        times.append(time.perf_counter() - t)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    return statistics.median(times), out
+
+
+def next_sparse_decode(torch, mv, batch, nsplit=16, heads=64, topk=512, replicas=64, seed=31, with_cpu=True):
+    """Sparse top-k MLA decode (one query token, 64 heads, 512 selected latent
+    rows per request) over a 2 GiB pool; each replica selects its own random
+    slots, so most rows come from HBM rather than the 256 MB Infinity Cache."""
+    import oracle.spec_ops_oracle as so
+
+    pool_rows = (2 << 30) // KV_ROW_BYTES
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    pool = torch.randn((pool_rows, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((batch, heads, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    idx = [torch.randperm(pool_rows, generator=gen, device="cuda")[:batch * topk].view(batch, topk).to(torch.int32)
+           for _ in range(replicas)]
+    out = torch.empty((batch, heads, V_DIM), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((batch, heads), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(192.0)
+    ws = mv.alloc_sparse_workspace(mv.sparse_desc(q, pool, idx[0], nsplit=nsplit, sm_scale=scale))
+    us = graph_us_per_call(torch, [lambda r=r: mv.sparse_decode(q, pool, idx[r], None, out, lse, ws, nsplit=nsplit,
+                                                                 sm_scale=scale) for r in range(replicas)])
+    mv.sparse_decode(q, pool, idx[0], None, out, lse, ws, nsplit=nsplit, sm_scale=scale)
+    torch.cuda.synchronize()
+    # parity of replica 0 on its gathered rows (the same definition, rows renumbered)
+    rows = pool[idx[0].long().flatten()].view(torch.int16).cpu().numpy().view(np.uint16)
+    local = np.arange(batch * topk, dtype=np.int32).reshape(batch, topk)
+    qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    keys = batch * topk
+    alg = keys * KV_ROW_BYTES + keys * 4 + batch * heads * (KV_ROW_BYTES + V_DIM * 2 + 4)
+    e = dict(row="sparse top-k decode", workload=f"{batch} request(s), 1 query token, {heads} heads, top-k {topk}, "
+                                                   f"page size 1 over a 2 GiB pool, NSPLIT {nsplit}",
+             latency_us=round(us, 3), bytes_per_call=alg, achieved_gbs=round(alg / (us * 1e-6) / 1e9, 1),
+             bound="hbm", hbm_frac=round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    if with_cpu:
+        t, (ro, rl) = _cpu_time(lambda: so.sparse_decode(qb, rows, local, None, scale))
+        o = bf16_from_bits(torch, out.view(torch.int16).cpu().numpy().view(np.uint16)).float().numpy()
+        e["parity_vs_oracle"] = dict(out_max_abs=float(np.abs(o - ro).max()),
+                                     lse_max_abs=float(np.abs(lse.cpu().numpy() - rl).max()))
+        e["cpu_oracle_us"] = round(t * 1e6, 1)
+    del pool, idx
+    torch.cuda.empty_cache()
+    return e
+
+
+def next_indexer(torch, mv, batch, positions, heads=64, seed=41, with_cpu=True):
+    """fp8 indexer logits over a paged cache of 8,448-byte blocks; R replicas of
+    the blocks (R x bytes >= 1 GiB), each with its own block table."""
+    import oracle.spec_ops_oracle as so
+    from workloads.ops_gen import indexer_case
+
+    max_blocks = -(-positions // 64)
+    c = indexer_case(seed, batch=batch, heads=heads, max_blocks=max_blocks, seq_lens=[positions] * batch,
+                     spare_blocks=0)
+    nb = c.blocks.shape[0]
+    reps_data = max(1, math.ceil(ROTATE_BYTES / c.blocks.nbytes))
+    blocks = torch.from_numpy(c.blocks).cuda().repeat(reps_data, 1)
+    bts = [torch.from_numpy(np.where(c.block_table >= 0, c.block_table + r * nb, -1).astype(np.int32)).cuda()
+           for r in range(reps_data)]
+    q = torch.from_numpy(c.q).cuda()
+    w = torch.from_numpy(c.weights).cuda()
+    sl = torch.from_numpy(c.seq_lens).cuda()
+    logits = torch.empty((batch, max_blocks * 64), dtype=torch.float32, device="cuda")
+    us = graph_us_per_call(torch, [lambda r=r: mv.indexer_logits(q, w, blocks, bts[r], sl, logits)
+                                   for r in range(reps_data)])
+    mv.indexer_logits(q, w, blocks, bts[0], sl, logits)
+    torch.cuda.synchronize()
+    pages = batch * max_blocks
+    alg = pages * (8448 + 4) + batch * max_blocks * 64 * 4 + batch * heads * (128 + 4) + batch * 4
+    flops = batch * positions * heads * 128 * 2
+    e = dict(row="fp8 indexer logits", workload=f"{batch} request(s) x {positions} positions, {heads} heads x 128 "
+                                                 f"e4m3, 8,448-byte blocks",
+             latency_us=round(us, 3), bytes_per_call=alg, achieved_gbs=round(alg / (us * 1e-6) / 1e9, 1),
+             bound="hbm", hbm_frac=round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+             mfma_frac=round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5))
+    if with_cpu:
+        t, ref = _cpu_time(lambda: so.indexer_logits(c.q, c.weights, c.blocks, c.block_table, c.seq_lens), max_reps=1)
+        mag = so.indexer_magnitude(c.q, c.weights, c.blocks, c.block_table, c.seq_lens)
+        got = logits.cpu().numpy()
+        fin = np.isfinite(ref)
+        # error over the fp32 terms' magnitude sum_h |w_h| sum_d |q k| s (the tests allow 2e-6)
+        e["parity_vs_oracle"] = dict(max_err_over_term_magnitude=float(np.max(np.abs(got[fin] - ref[fin]) /
+                                                                               np.maximum(mag[fin], 1e-30))),
+                                     neg_inf_positions_match=bool(np.array_equal(np.isfinite(got), fin)))
+        e["cpu_oracle_us"] = round(t * 1e6, 1)
+    del blocks
+    torch.cuda.empty_cache()
+    return e
+
+
+def next_accept_commit(torch, mv, batch, nodes, tree, seed=51, with_cpu=True):
+    """The step around verify: the draft rows' KV append, the greedy tree
+    accept and the commit of the accepted path, as one captured sequence."""
+    import oracle.spec_ops_oracle as so
+    from workloads.ops_gen import accept_case
+
+    c = accept_case(seed, batch=batch, nodes=nodes, tree=tree, match=0.85)
+    rng = np.random.default_rng(seed)
+    kv = torch.randn((c.num_slots, QK_DIM), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    rows_np = rng.integers(0, 65535, size=(batch * nodes, QK_DIM), dtype=np.uint16)
+    rows = bf16_from_bits(torch, rows_np).cuda()
+    loc_np = np.concatenate([c.page_table[b, c.seq_lens[b] - nodes:c.seq_lens[b]] for b in range(batch)])
+    loc = torch.from_numpy(loc_np.astype(np.int32)).cuda()
+    pt0 = torch.from_numpy(c.page_table).cuda()
+    pt = pt0.clone()
+    par, drf, tgt = (torch.from_numpy(x).cuda() for x in (c.tree_parent, c.draft_tokens, c.target_tokens))
+    sl = torch.from_numpy(c.seq_lens).cuda()
+    n = torch.empty(batch, dtype=torch.int32, device="cuda")
+    path = torch.empty((batch, nodes), dtype=torch.int32, device="cuda")
+    com = torch.empty((batch, nodes), dtype=torch.int32, device="cuda")
+    ctx = torch.empty(batch, dtype=torch.int32, device="cuda")
+    freed = torch.empty((batch, nodes), dtype=torch.int32, device="cuda")
+
+    def step():
+        pt.copy_(pt0)
+        mv.kv_append(kv, rows, loc)
+        mv.tree_accept(par, drf, tgt, n, path, com)
+        mv.commit_accepted(pt, sl, nodes, n, path, ctx, freed)
+
+    us = graph_us_per_call(torch, [step] * 16)
+    step()
+    torch.cuda.synchronize()
+    alg = batch * nodes * (2 * KV_ROW_BYTES + 4) + batch * nodes * 4 * 6 + batch * 4 * 3
+    e = dict(row="KV append + tree accept + commit", workload=f"{batch} request(s), {nodes}-node {tree} trees, "
+                                                                 f"page size 1",
+             latency_us=round(us, 3), bytes_per_call=alg, achieved_gbs=round(alg / (us * 1e-6) / 1e9, 2),
+             bound="latency")
+    if with_cpu:
+        def cpu():
+            rn, rp, rc = so.tree_accept(c.tree_parent, c.draft_tokens, c.target_tokens)
+            return rn, rp, rc, so.commit_accepted(c.page_table, c.seq_lens, nodes, rn, rp)
+        t, (rn, rp, rc, (rpt, rctx, rfreed, _)) = _cpu_time(cpu)
+        e["parity_vs_oracle"] = dict(bit_exact=bool(
+            np.array_equal(n.cpu().numpy(), rn) and np.array_equal(path.cpu().numpy(), rp) and
+            np.array_equal(com.cpu().numpy(), rc) and np.array_equal(pt.cpu().numpy(), rpt) and
+            np.array_equal(ctx.cpu().numpy(), rctx) and np.array_equal(freed.cpu().numpy(), rfreed)))
+        e["mean_commit_len"] = float(rn.mean())
+        e["cpu_oracle_us"] = round(t * 1e6, 1)
+    return e
+
+
+def next_window_map(torch, mv, batch=8, window=4096, page=64, seed=61, with_cpu=True):
+    """The page-aligned sliding-window slot map of a draft cache (W = 4096,
+    P = 64), lengths log-uniform in [1k, 128k]."""
+    import oracle.spec_ops_oracle as so
+    from workloads.ops_gen import window_case
+
+    tm_np, lens_np = window_case(seed, batch=batch, width=131_072, lo=1024, hi=131_072)
+    tm = torch.from_numpy(tm_np).cuda()
+    lens = torch.from_numpy(lens_np).cuda()
+    dm = torch.empty((batch, window + page - 1), dtype=torch.int32, device="cuda")
+    cl = torch.empty(batch, dtype=torch.int32, device="cuda")
+    us = graph_us_per_call(torch, [lambda: mv.window_map(tm, lens, window, page, dm, cl)] * 64)
+    mv.window_map(tm, lens, window, page, dm, cl)
+    torch.cuda.synchronize()
+    alg = int(sum(so.compact_len(int(x), window, page) for x in lens_np)) * 4 + batch * (window + page - 1) * 4 + batch * 8
+    e = dict(row="sliding-window slot map", workload=f"{batch} requests, W {window}, P {page}, lengths log-uniform "
+                                                       f"in [1k, 128k]",
+             latency_us=round(us, 3), bytes_per_call=alg, achieved_gbs=round(alg / (us * 1e-6) / 1e9, 2),
+             bound="latency")
+    if with_cpu:
+        t, (rdm, rcl) = _cpu_time(lambda: so.window_map(tm_np, lens_np, window, page))
+        e["parity_vs_oracle"] = dict(bit_exact=bool(np.array_equal(dm.cpu().numpy(), rdm) and
+                                                     np.array_equal(cl.cpu().numpy(), rcl)))
+        e["cpu_oracle_us"] = round(t * 1e6, 1)
+    return e
+
+
+def measure_next_rows(torch, mv, with_cpu=True):
+    rows = []
+    for fn, kw in [(next_sparse_decode, dict(batch=1, nsplit=16)), (next_sparse_decode, dict(batch=16, nsplit=8)),
+                   (next_accept_commit, dict(batch=8, nodes=12, tree="chain")),
+                   (next_accept_commit, dict(batch=1, nodes=32, tree="depth8")),
+                   (next_window_map, dict()),
+                   (next_indexer, dict(batch=1, positions=262_208)), (next_indexer, dict(batch=16, positions=32_768))]:
+        e = fn(torch, mv, with_cpu=with_cpu, **kw)
+        log(f"next row {e['row']}: {e['workload']}: {e['latency_us']} us")
+        rows.append(e)
+    return rows
+
+
 # ---------------------------------------------------------------- main
 
 def measure_case(torch, mv, case, nsplit, steps, warmup, seed):
@@ -392,6 +600,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--full-sweep", action="store_true", help="contexts from 1k to 184,728 (27 points)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the rows next to verify (sparse decode, accept/"
+                                                            "commit, window map, fp8 indexer)")
     ap.add_argument("--seed", type=int, default=1234)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -469,6 +679,9 @@ def main():
         o = bf16_bits_to_f64(gpu_out)
         line["parity_vs_oracle"] = dict(out_max_abs=float(np.abs(o - ref[0]).max()),
                                         lse_max_abs=float(np.abs(gpu_lse - ref[1]).max()))
+
+    if not args.no_next:
+        line["next_rows"] = measure_next_rows(torch, mv, with_cpu=not args.no_cpu)
 
     if not args.no_sweep:
         sweep = []

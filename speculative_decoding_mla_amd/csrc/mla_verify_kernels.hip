@@ -267,7 +267,10 @@ constexpr int kPassAdaptive = 0;  // accumulate; reference = first visible tile 
 constexpr int kPassMaxOnly = 1;   // scores only: exact row max over the split
 constexpr int kPassFixed = 2;     // accumulate against a given reference
 
-template <int NW>
+// kSparse: one query token per request over an index list (sparse top-k
+// decode): lengths may be absent, an entry of -1 is unused, every node is a
+// root. A compile-time switch, so the verify instantiations carry none of it.
+template <int NW, bool kSparse>
 __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch L) {
   constexpr int kInstrPerWave = kTileInstr / NW;
   static_assert(kTileInstr % NW == 0, "tile loads must split evenly over the waves");
@@ -299,8 +302,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int nsplit_b = __builtin_amdgcn_readfirstlane(sr.count);
 
   const int T = L.nodes;
-  const int n_raw = raw_len(L, b);
-  const int n = min(max(n_raw, L.min_len), L.capacity);
+  const int n_raw = kSparse ? raw_len(L, b) : L.seq_lens[b];
+  const int n = min(max(n_raw, kSparse ? 0 : T), L.capacity);
   if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
   const int ctx = n - T;
   const int chunk = (n + nsplit_b - 1) / nsplit_b;
@@ -538,16 +541,15 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
         if (!ok) {
           atomicOr(&badbits_s[i >> 5], 1u << (i & 31));
           // an unused entry (-1) of a sparse index list is masked quietly
-          if (!(L.quiet_unused && page == -1)) bad = 1;
+          if (!(kSparse && page == -1)) bad = 1;
         }
       }
       const int wave_bad = __any(bad);
       if (lane == 0) badw_s[wid] = wave_bad;
       if (kMode == kPassAdaptive && need_mask && w0 == k0 && wid == 0) {
-        // without a parent array every node is a root (one query token per request)
-        const uint64_t a = L.tree_parent != nullptr
-                               ? ancestor_bits(L.tree_parent + static_cast<size_t>(b) * T, T, lane, L.err)
-                               : (lane < T ? 1ull << lane : 0ull);
+        // sparse decode: every node is a root (one query token per request)
+        const uint64_t a = kSparse ? (lane < T ? 1ull << lane : 0ull)
+                                   : ancestor_bits(L.tree_parent + static_cast<size_t>(b) * T, T, lane, L.err);
         anc_s[lane] = a;
       }
       lds_barrier();
@@ -841,15 +843,23 @@ hipError_t launch_tree_mask(const int32_t* tree_parent, uint64_t* anc, int batch
   return hipGetLastError();
 }
 
-hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream) {
+template <bool kSparse>
+void launch_partial_t(const VerifyLaunch& L, hipStream_t stream) {
   const int total = L.batch * L.nsplit * L.row_blocks;
   const int grid = (total + 7) / 8 * 8;
   switch (L.waves_per_wg) {
-    case 1: hipLaunchKernelGGL(verify_partial_kernel<1>, dim3(grid), dim3(64), 0, stream, L); break;
-    case 2: hipLaunchKernelGGL(verify_partial_kernel<2>, dim3(grid), dim3(128), 0, stream, L); break;
-    case 3: hipLaunchKernelGGL(verify_partial_kernel<3>, dim3(grid), dim3(192), 0, stream, L); break;
-    default: hipLaunchKernelGGL(verify_partial_kernel<4>, dim3(grid), dim3(256), 0, stream, L); break;
+    case 1: hipLaunchKernelGGL((verify_partial_kernel<1, kSparse>), dim3(grid), dim3(64), 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((verify_partial_kernel<2, kSparse>), dim3(grid), dim3(128), 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((verify_partial_kernel<3, kSparse>), dim3(grid), dim3(192), 0, stream, L); break;
+    default: hipLaunchKernelGGL((verify_partial_kernel<4, kSparse>), dim3(grid), dim3(256), 0, stream, L); break;
   }
+}
+
+hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream) {
+  if (L.quiet_unused)
+    launch_partial_t<true>(L, stream);
+  else
+    launch_partial_t<false>(L, stream);
   return hipGetLastError();
 }
 
