@@ -10,9 +10,15 @@ sit in disjoint regions of one pool (R x KV bytes >= 1 GiB); every replica
 holds the same logical rows, so every step computes the same result. The R
 calls are captured in one hipGraph and replayed.
 
-Prints one JSON line. Options: --workload (C1, C2, C3, C4a, C4b, C5, or a
-sweep point S<context>_T<nodes>[_contig]), --nsplit, --steps, --warmup,
---no-sweep, --full-sweep, --no-cpu.
+Prints one JSON line. Options: --workload (C1, C2, C3, C4a, C4b, C5, a sweep
+point S<context>_T<nodes>[_contig], or one of the rows next to verify, F1_* to
+F4_*), --nsplit, --steps, --warmup, --no-sweep, --full-sweep, --no-cpu,
+--no-next.
+
+The default line also carries next_rows: the steps next to verify (sparse
+top-k decode, KV append + tree accept + commit, the sliding-window slot map,
+the fp8 indexer), each timed from graph replays, with its parity against the
+oracle and the oracle's host time.
 """
 
 from __future__ import annotations
@@ -39,6 +45,8 @@ KV_ROW_BYTES = QK_DIM * 2  # one bf16 latent row per key
 ROTATE_BYTES = 1 << 30     # >= 4 x the 256 MB Infinity Cache
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_mla_amd", "csrc", "mla_verify_kernels.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "verify_partial_C2_hbm_traffic.md")
+OPS_SOURCE = os.path.join(ROOT, "speculative_decoding_mla_amd", "csrc", "mla_spec_ops.hip")
+INDEXER_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_F3_B1_262208_hbm_traffic.md")
 # Context-sweep grid (contexts x tree sizes); --full-sweep adds the short contexts.
 SWEEP = [(c, t) for c in (4_096, 16_384, 65_536, 131_072, 184_728) for t in (9, 16, 32)]
 FULL_SWEEP = [(c, t) for c in (1_024, 2_048, 4_096, 8_192, 16_384, 32_768, 65_536, 131_072, 184_728)
@@ -107,24 +115,24 @@ def default_nsplit(batch, nodes, heads, max_keys) -> int:
     return int(max(1, min(per_req, max_keys // 256 if max_keys >= 256 else 1)))
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the partial kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel
-    calibration). Returns None unless the summary was taken on this workload
-    from the kernel source as it is now."""
+def measured_traffic(workload: str, profile: str = TRAFFIC_PROFILE, source: str = KERNEL_SOURCE):
+    """HBM bytes per launch of a kernel from a committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel calibration).
+    Returns None unless the summary was taken on this workload from the kernel
+    source as it is now."""
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(profile) as f:
             fields = dict(ln.split(":", 1) for ln in f if ln.startswith(("traffic_", "kernel_source_sha256", "workload")))
     except OSError:
         return None
     fields = {k.strip(): v.strip() for k, v in fields.items()}
-    if fields.get("kernel_source_sha256") != kernel_source_digest() or fields.get("workload") != workload:
+    if fields.get("kernel_source_sha256") != kernel_source_digest(source) or fields.get("workload") != workload:
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -429,7 +437,8 @@ def next_indexer(torch, mv, batch, positions, heads=64, seed=41, with_cpu=True):
                                                  f"e4m3, 8,448-byte blocks",
              latency_us=round(us, 3), bytes_per_call=alg, achieved_gbs=round(alg / (us * 1e-6) / 1e9, 1),
              bound="hbm", hbm_frac=round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-             mfma_frac=round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5))
+             mfma_frac=round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 5),
+             traffic=measured_traffic(f"F3_indexer_B{batch}_{positions}", INDEXER_TRAFFIC_PROFILE, OPS_SOURCE))
     if with_cpu:
         t, ref = _cpu_time(lambda: so.indexer_logits(c.q, c.weights, c.blocks, c.block_table, c.seq_lens), max_reps=1)
         mag = so.indexer_magnitude(c.q, c.weights, c.blocks, c.block_table, c.seq_lens)
@@ -523,15 +532,25 @@ def next_window_map(torch, mv, batch=8, window=4096, page=64, seed=61, with_cpu=
     return e
 
 
-def measure_next_rows(torch, mv, with_cpu=True):
+NEXT_ROWS = {
+    "F1_sparse_B1": (next_sparse_decode, dict(batch=1, nsplit=16)),
+    "F1_sparse_B16": (next_sparse_decode, dict(batch=16, nsplit=8)),
+    "F2_accept_B8_chain12": (next_accept_commit, dict(batch=8, nodes=12, tree="chain")),
+    "F2_accept_B1_tree32": (next_accept_commit, dict(batch=1, nodes=32, tree="depth8")),
+    "F4_window_B8": (next_window_map, dict()),
+    "F3_indexer_B1_262208": (next_indexer, dict(batch=1, positions=262_208)),
+    "F3_indexer_B16_32768": (next_indexer, dict(batch=16, positions=32_768)),
+}
+
+
+def measure_next_rows(torch, mv, with_cpu=True, only=None):
     rows = []
-    for fn, kw in [(next_sparse_decode, dict(batch=1, nsplit=16)), (next_sparse_decode, dict(batch=16, nsplit=8)),
-                   (next_accept_commit, dict(batch=8, nodes=12, tree="chain")),
-                   (next_accept_commit, dict(batch=1, nodes=32, tree="depth8")),
-                   (next_window_map, dict()),
-                   (next_indexer, dict(batch=1, positions=262_208)), (next_indexer, dict(batch=16, positions=32_768))]:
+    for name, (fn, kw) in NEXT_ROWS.items():
+        if only is not None and name != only:
+            continue
         e = fn(torch, mv, with_cpu=with_cpu, **kw)
-        log(f"next row {e['row']}: {e['workload']}: {e['latency_us']} us")
+        e["name"] = name
+        log(f"next row {name}: {e['workload']}: {e['latency_us']} us")
         rows.append(e)
     return rows
 
@@ -595,7 +614,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--workload", default="C2",
-                    help="C1, C2, C3, C4a, C4b, C5, or a context-sweep point S<context>_T<nodes>[_contig]")
+                    help="C1, C2, C3, C4a, C4b, C5, a context-sweep point S<context>_T<nodes>[_contig], or one "
+                         "row next to verify: " + ", ".join(NEXT_ROWS))
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--full-sweep", action="store_true", help="contexts from 1k to 184,728 (27 points)")
@@ -616,6 +636,10 @@ def main():
     from workloads import make_case
 
     mv.load_library()
+    if args.workload in NEXT_ROWS:
+        e = measure_next_rows(torch, mv, with_cpu=not args.no_cpu, only=args.workload)[0]
+        print(json.dumps(dict(metric=METRIC, n_gpus=1, next_rows=[e])), flush=True)
+        return
     if args.workload.startswith("S"):
         spec = args.workload[1:].split("_")
         ctx, nodes = int(spec[0]), int(spec[1][1:])
