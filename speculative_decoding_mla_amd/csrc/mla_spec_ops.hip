@@ -8,9 +8,10 @@
 // draft tree (at most 64 nodes) done inside one wave by pointer jumping. The
 // indexer is a small dense contraction per cache block (64 positions x 64
 // heads x 128 dims): its fp8 operands are widened exactly to bf16 and fed to
-// v_mfma_f32_32x32x16_bf16 straight from global memory, and the ReLU /
-// weight / head-sum / scale epilogue runs through LDS. Every grid is fixed by
-// host-known sizes; blocks past a request's length exit after writing -inf.
+// v_mfma_f32_32x32x16_bf16 straight from global memory by persistent
+// workgroups, and the ReLU / weight / head-sum / scale epilogue stays in
+// registers. Every grid is fixed by host-known sizes; blocks past a request's
+// length are written -inf without being read.
 
 #include <hip/hip_runtime.h>
 
@@ -29,6 +30,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowChunks = 72;  // 16-byte chunks of a 1,152-byte latent row
+constexpr int kIndexerGrid = 512;  // persistent indexer workgroups: two per CU (two waves per SIMD at 142 VGPRs)
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bit) {
   if (err != nullptr) atomicOr(err, bit);
@@ -253,69 +255,168 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 constexpr int kIdxPage = 64, kIdxDim = 128, kIdxBlockBytes = 8448, kIdxScaleOff = kIdxPage * kIdxDim;
 
-// One workgroup of four waves per (request, block). Wave w computes the
-// 32 x 32 tile (positions 32 (w & 1) + 0..31) x (heads 32 (w >> 1) + 0..31) of
-// K Q^T with eight MFMAs. The contraction index is permuted the same way on
-// both sides: k-step ks and lane half hs cover dims 64 hs + 8 ks + 0..7, so
-// each lane's operand bytes for all eight steps are 64 contiguous bytes of its
-// position's row (A) and its head's row (B).
+// Sum of v[0..15] over the 32 lanes of each wave half, by halving: at the step
+// with lane bit m, a lane keeps the half of its values its bit selects, and
+// adds the partner's copy of that half (one shuffle per kept value). After the
+// four steps m = 16, 8, 4, 2 a lane holds element 8 b4 + 4 b3 + 2 b2 + b1 (bits
+// of lane % 32) summed over 16 lanes; the step m = 1 completes the 32 lanes.
+// 16 shuffles in all instead of 80.
+__device__ __forceinline__ float head_sum_halving(const float (&v)[16], int lane) {
+  float a8[8], a4[4], a2[2];
+  {
+    const bool up = lane & 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a8[i] = (up ? v[i + 8] : v[i]) + __shfl_xor(up ? v[i] : v[i + 8], 16);
+  }
+  {
+    const bool up = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a4[i] = (up ? a8[i + 4] : a8[i]) + __shfl_xor(up ? a8[i] : a8[i + 4], 8);
+  }
+  {
+    const bool up = lane & 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a2[i] = (up ? a4[i + 2] : a4[i]) + __shfl_xor(up ? a4[i] : a4[i + 2], 4);
+  }
+  const bool up = lane & 2;
+  const float a1 = (up ? a2[1] : a2[0]) + __shfl_xor(up ? a2[0] : a2[1], 2);
+  return a1 + __shfl_xor(a1, 1);
+}
+
+// Persistent waves, independent of each other (no barrier, no LDS): the
+// work unit is half a block, 32 positions x all 64 heads. Wave g of the grid
+// streams a contiguous run of units of the flattened (request, block, half)
+// space: the run's block ids, lengths and requests are read once (one lane per
+// unit), the request's queries are widened to bf16 once and stay in
+// registers, and the next unit's 4 KiB are loaded while the current one is
+// multiplied. A unit is two 32 x 32 tiles of K Q^T (head halves) over the same
+// K fragments: 16 MFMAs. The contraction index is permuted the same way on
+// both sides (k-step ks and lane half hs cover dims 64 hs + 8 ks + 0..7), so a
+// lane's operand bytes are 64 contiguous bytes of its row. The ReLU, the head
+// weights and the sum over the 64 heads stay in registers (head_sum_halving).
 __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
-  __shared__ float red[4][32][33];  // [wave][position][head], padded against bank conflicts
-  const int b = blockIdx.y;
-  const int page = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int hs = lane >> 5;
-  const int raw = I.seq_lens[b];
   const int cap = I.max_blocks * kIdxPage;
-  const int n = min(max(raw, 0), cap);
-  if (raw != n && page == 0 && tid == 0) flag(I.err, MLA_DEVERR_SEQ_LEN);
-  float* out = I.logits + static_cast<size_t>(b) * cap + static_cast<size_t>(page) * kIdxPage;
-  const int pos0 = page * kIdxPage;
-  if (pos0 >= n) {  // past the request's length: nothing to read
-    if (tid < kIdxPage) out[tid] = -INFINITY;
-    return;
+  const int units = I.batch * I.max_blocks * 2;
+  const int waves = static_cast<int>(gridDim.x) * (blockDim.x >> 6);
+  const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int per = (units + waves - 1) / waves;  // <= 64 (host)
+  const int first = gw * per;
+  const int cnt = min(units, first + per) - first;
+  if (cnt <= 0) return;
+
+  // lane k < cnt describes unit `first + k`: request, clamped length, block id
+  // (-1 past the length, -2 out of range)
+  // The table entry is read together with the length (the table is in bounds
+  // whatever the length; an entry past it is never used), so the block ids
+  // are one round trip away, not two.
+  int my_b = 0, my_n = 0, my_blk = -1;
+  if (lane < cnt) {
+    const int u = first + lane;
+    my_b = u / (2 * I.max_blocks);
+    const int page = (u >> 1) - my_b * I.max_blocks;
+    const int raw = I.seq_lens[my_b];
+    const int entry = I.block_table[u >> 1];
+    my_n = min(max(raw, 0), cap);
+    if (raw != my_n && page == 0 && (u & 1) == 0) flag(I.err, MLA_DEVERR_SEQ_LEN);
+    if (page * kIdxPage + (u & 1) * 32 < my_n) {
+      my_blk = entry;
+      if (my_blk < 0 || my_blk >= I.num_blocks) {
+        flag(I.err, MLA_DEVERR_SLOT_RANGE);
+        my_blk = -2;
+      }
+    }
   }
-  const int32_t blk = I.block_table[static_cast<size_t>(b) * I.max_blocks + page];
-  if (blk < 0 || blk >= I.num_blocks) {
-    if (tid == 0) flag(I.err, MLA_DEVERR_SLOT_RANGE);
-    if (tid < kIdxPage) out[tid] = -INFINITY;
-    return;
-  }
-  const uint8_t* block = I.kv_blocks + static_cast<size_t>(blk) * kIdxBlockBytes;
-  const int pb = w & 1, hb = w >> 1;
-  const int pos = pb * 32 + (lane & 31);
-  const int head = hb * 32 + (lane & 31);
-  const bool head_ok = head < I.heads;
-  const u32x4* arow = reinterpret_cast<const u32x4*>(block + pos * kIdxDim + hs * 64);
-  const u32x4* brow = reinterpret_cast<const u32x4*>(I.q + (static_cast<size_t>(b) * I.heads + (head_ok ? head : 0)) * kIdxDim + hs * 64);
-  u32x4 av[4], bv[4];
+
+  const int hd = lane & 31;  // this lane's head in each half, and its row of the K tile
+  // the position whose head sum this lane ends up holding (head_sum_halving)
+  const int j_sum = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
+  const int r_sum = 8 * (j_sum >> 2) + 4 * hs + (j_sum & 3);
+  // A unit's bytes (this lane's 64 bytes of the K tile, and the scale of the
+  // position it will hold) are loaded kAhead units before they are used;
+  // loads retire in issue order, so nothing that waits on a unit's bytes also
+  // waits on a later unit's.
+  constexpr int kAhead = 2;
+  struct UnitBytes {
+    u32x4 k[4];
+    float scale;
+  };
+  auto load_unit = [&](int kk, UnitBytes& dst) {
+    const int blk = __shfl(my_blk, kk);
+    if (kk < cnt && blk >= 0) {
+      const uint8_t* block = I.kv_blocks + static_cast<size_t>(blk) * kIdxBlockBytes;
+      const int half = (first + kk) & 1;
+      dst.scale = reinterpret_cast<const float*>(block + kIdxScaleOff)[half * 32 + r_sum];
+      const u32x4* a = reinterpret_cast<const u32x4*>(block + (half * 32 + hd) * kIdxDim + hs * 64);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    av[i] = arow[i];
-    bv[i] = head_ok ? brow[i] : u32x4{0u, 0u, 0u, 0u};
-  }
-  f32x16 acc = {};
+      for (int i = 0; i < 4; ++i) dst.k[i] = a[i];
+    }
+  };
+
+  int cur_b = -1;
+  bf16x8 q0[8], q1[8];
+  float w0 = 0.f, w1 = 0.f;
+  auto process = [&](int kk, const UnitBytes& ub) {
+    const int u = first + kk;
+    const int b = __shfl(my_b, kk);
+    const int n = __shfl(my_n, kk);
+    const int blk = __shfl(my_blk, kk);
+    const int page = (u >> 1) - b * I.max_blocks;
+    const int pos0 = page * kIdxPage + (u & 1) * 32;
+    float* out = I.logits + static_cast<size_t>(b) * cap + pos0;
+    if (blk < 0) {  // past the length, or an out-of-range block: nothing to read
+      if (lane < 32) out[lane] = -INFINITY;
+      return;
+    }
+    if (b != cur_b) {  // a new request: its queries (widened once) and head weights
+      cur_b = b;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const u32x4& a = av[ks >> 1];
-    const u32x4& q = bv[ks >> 1];
-    const int o = (ks & 1) * 2;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16(a[o], a[o + 1]), e4m3x8_to_bf16(q[o], q[o + 1]),
-                                                   acc, 0, 0, 0);
-  }
-  // lane holds C[r][lane % 32] for r = 8 (j / 4) + 4 hs + j % 4: ReLU, head weight
-  const float wt = head_ok ? I.weights[static_cast<size_t>(b) * I.heads + head] : 0.f;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int head = h2 * 32 + hd;
+        const bool ok = head < I.heads;
+        const u32x4* qrow = reinterpret_cast<const u32x4*>(
+            I.q + (static_cast<size_t>(b) * I.heads + (ok ? head : 0)) * kIdxDim + hs * 64);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) red[w][8 * (j >> 2) + 4 * hs + (j & 3)][lane & 31] = wt * fmaxf(acc[j], 0.f);
-  __syncthreads();
-  if (tid < kIdxPage) {
-    const int p = tid;  // position in the block
-    const int pbl = p >> 5, r = p & 31;
-    float s = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < 32; ++c) s += red[pbl][r][c] + red[pbl + 2][r][c];
-    const float scale = reinterpret_cast<const float*>(block + kIdxScaleOff)[p];
-    out[p] = pos0 + p < n ? s * scale : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 qq = ok ? qrow[i] : u32x4{0u, 0u, 0u, 0u};
+          bf16x8(&qd)[8] = h2 == 0 ? q0 : q1;
+          qd[2 * i] = e4m3x8_to_bf16(qq[0], qq[1]);
+          qd[2 * i + 1] = e4m3x8_to_bf16(qq[2], qq[3]);
+        }
+        const float wv = ok ? I.weights[static_cast<size_t>(b) * I.heads + head] : 0.f;
+        if (h2 == 0) w0 = wv; else w1 = wv;
+      }
+    }
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4& a = ub.k[ks >> 1];
+      const int o = (ks & 1) * 2;
+      const bf16x8 kb = e4m3x8_to_bf16(a[o], a[o + 1]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, q0[ks], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, q1[ks], acc1, 0, 0, 0);
+    }
+    // lane holds C[r][head] for r = 8 (j / 4) + 4 hs + j % 4 in both head halves
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = w0 * fmaxf(acc0[j], 0.f) + w1 * fmaxf(acc1[j], 0.f);
+    const float sum = head_sum_halving(v, lane);
+    if ((lane & 1) == 0) out[r_sum] = pos0 + r_sum < n ? sum * ub.scale : -INFINITY;
+  };
+
+  // ring of kAhead + 1 units, unrolled so that every ring index is a constant
+  UnitBytes ring[kAhead + 1];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) load_unit(i, ring[i]);
+  for (int k = 0; k < cnt; k += kAhead + 1) {
+#pragma unroll
+    for (int slot = 0; slot <= kAhead; ++slot) {
+      if (k + slot < cnt) {
+        load_unit(k + slot + kAhead, ring[(slot + kAhead) % (kAhead + 1)]);
+        process(k + slot, ring[slot]);
+      }
+    }
   }
 }
 
@@ -352,7 +453,13 @@ hipError_t launch_window_map(const int32_t* target_map, int map_stride, const in
 }
 
 hipError_t launch_indexer(const IndexerLaunch& I, hipStream_t stream) {
-  hipLaunchKernelGGL(indexer_kernel, dim3(I.max_blocks, I.batch), dim3(256), 0, stream, I);
+  // persistent waves (four per workgroup, all resident), each over at most 64 consecutive half-blocks
+  const int64_t units = static_cast<int64_t>(I.batch) * I.max_blocks * 2;
+  int64_t waves = (units + 63) / 64;
+  if (waves < 4 * kIndexerGrid) waves = 4 * kIndexerGrid;
+  if (waves > units) waves = units;
+  const int64_t grid = (waves + 3) / 4;
+  hipLaunchKernelGGL(indexer_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, I);
   return hipGetLastError();
 }
 
