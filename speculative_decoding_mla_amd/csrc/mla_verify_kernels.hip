@@ -106,6 +106,15 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane from global memory straight into LDS at m0 + 4*lane (lanes
+// outside exec write nothing).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 // Same, from a wave-uniform base address plus a per-lane 32-bit offset.
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -225,11 +234,12 @@ __device__ SplitRange split_plan(const VerifyLaunch& L, int key, bool by_slot, i
 // jumping: after round r a node's mask covers ancestors closer than 2^r and its
 // pointer names the ancestor 2^r up. Six rounds cover 64 nodes. The whole wave
 // must call it. A parent outside [-1, lane) is reported and replaced by -1.
-__device__ uint64_t ancestor_bits(const int32_t* parents, int T, int lane, uint32_t* err) {
+// `parent` is parents[lane] for lane < T (ignored above).
+__device__ uint64_t ancestor_bits_of(int parent, int T, int lane, uint32_t* err) {
   int p = -1;
   bool bad = false;
   if (lane < T) {
-    p = parents[lane];
+    p = parent;
     if (p < -1 || p >= lane) {
       bad = true;
       p = -1;
@@ -248,6 +258,9 @@ __device__ uint64_t ancestor_bits(const int32_t* parents, int T, int lane, uint3
   }
   if (__any(bad) && lane == 0 && err != nullptr) atomicOr(err, MLA_DEVERR_BAD_PARENT);
   return anc;
+}
+__device__ uint64_t ancestor_bits(const int32_t* parents, int T, int lane, uint32_t* err) {
+  return ancestor_bits_of(lane < T ? parents[lane] : -1, T, lane, err);
 }
 
 __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict__ parents,
@@ -278,6 +291,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 
   __shared__ __attribute__((aligned(1024))) uint8_t kv_s[kStages * kTileBytes];
   __shared__ int32_t slot_s[kSlotCap];
+  __shared__ int32_t pt_s[kSlotCap / 2 + 1];  // page-table entries of a window of pages of 2+ keys
   __shared__ uint32_t badbits_s[kTilesPerWindow];  // bit k: key k of the tile sits on a bad slot
   __shared__ uint64_t anc_s[kMaxNodes];
   __shared__ int32_t badw_s[NW];
@@ -302,7 +316,44 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int nsplit_b = __builtin_amdgcn_readfirstlane(sr.count);
 
   const int T = L.nodes;
+  const int row = rb * (NW * 32) + wid * 32 + (lane & 31);
+  const bool row_ok = row < L.rows;
+
+  // The chain before the first key tile is length -> page table -> keys;
+  // the tree parents (wave 0) and the query rows are requested beside it.
   const int n_raw = kSparse ? raw_len(L, b) : L.seq_lens[b];
+  int parent = -1;
+  if (!kSparse && wid == 0 && lane < T) parent = L.tree_parent[static_cast<size_t>(b) * T + lane];
+
+  const uint32_t lds_kv = lds_addr(kv_s);
+  const uint32_t lane16 = lane * 16;
+
+  // This wave's 32 query rows go to KV stage `wid` in the layout of a key
+  // tile (row k of the wave in the place of key k), with the same
+  // line-coalesced global->LDS loads; each lane then reads its B operands of
+  // S^T = K Q^T from there exactly as it reads K fragments. (Loaded straight
+  // into registers, every load instruction would gather 32 bytes from each
+  // of 32 rows, and the rows of four waves do not fit the L1: each line came
+  // from L2 four times over.) Padding rows load row 0 of the request; their
+  // results are never stored.
+  {
+    const int r0 = rb * (NW * 32) + wid * 32;  // wave-uniform
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(L.q) + static_cast<size_t>(b) * L.rows * kRowBytes;
+    const uint32_t stage = lds_kv + wid * kTileBytes;
+#pragma unroll 4
+    for (int k = 0; k < kKeysPerTile; ++k) {
+      const int r = r0 + k < L.rows ? r0 + k : 0;
+      dma16_sbase(qb + static_cast<size_t>(r) * kRowBytes, lane16 ^ (swz(k) << 4), stage + k * kLatentBytes);
+    }
+#pragma unroll
+    for (int g = 0; g < kRopeInstr; ++g) {
+      const int k = 8 * g + (lane >> 3);
+      const int r = r0 + k < L.rows ? r0 + k : 0;
+      dma16(qb + static_cast<size_t>(r) * kRowBytes + ((kVDim / 8 + ((lane & 7) ^ swz(k))) << 4),
+            stage + kRopeBase + g * 1024);
+    }
+  }
+
   const int n = min(max(n_raw, kSparse ? 0 : T), L.capacity);
   if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
   const int ctx = n - T;
@@ -310,28 +361,33 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int k0 = s * chunk;
   const int k1 = min(n, k0 + chunk);
 
-  const int row = rb * (NW * 32) + wid * 32 + (lane & 31);
-  const bool row_ok = row < L.rows;
   f32x2* lse_dst = reinterpret_cast<f32x2*>(L.part_lse) + static_cast<size_t>(slot) * L.rows_pad + row;
   if (k0 >= k1) {  // empty split: contributes nothing
     if (lane < 32) *lse_dst = f32x2{-INFINITY, 0.f};
     return;
   }
 
-  // This wave's 32 query rows as B operands of S^T = K Q^T (k-step ks covers
-  // dims 16ks..16ks+15; lane holds dims 16ks + 8*hsel + 0..7 of row lane%32).
-  bf16x8 qf[kQSteps];
-  {
-    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(L.q) +
-                         (static_cast<size_t>(b) * L.rows + (row_ok ? row : 0)) * (kQkDim / 8);
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = row_ok ? qrow[2 * ks + hsel] : bf16x8{};
-  }
+  // Page-table entries of the keys [w0, w0 + wn), one wave-wide 4-byte
+  // global->LDS load per 64 entries: with one key per page straight into
+  // slot_s (each entry is then checked in place by the thread that owns its
+  // key), with larger pages into pt_s; the window's bad-key bits are cleared
+  // beside them. Pages pg0.. of the window lie below max_pages.
+  auto request_window = [&](int w0, int wn) {
+    const int pg0 = w0 >> L.page_shift;
+    const int npg = ((w0 + wn - 1) >> L.page_shift) - pg0 + 1;
+    const int32_t* pt = L.page_table + static_cast<size_t>(b) * L.max_pages + pg0;
+    const uint32_t pt_lds = lds_addr(L.page_shift == 0 ? slot_s : pt_s);
+    for (int j0 = wid * 64; j0 < npg; j0 += NW * 64)
+      if (j0 + lane < npg) dma4(pt + j0 + lane, pt_lds + j0 * 4);
+    const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
+    for (int i = threadIdx.x; i < ntiles; i += NW * 64) badbits_s[i] = 0u;
+  };
+  request_window(k0, min(k1 - k0, kSlotCap));
+
+  bf16x8 qf[kQSteps];  // lane: dims 16ks + 8*hsel + 0..7 of row lane%32
   const int node = row_ok ? row / L.heads : 0;
   const bool need_mask = k1 > ctx;
   uint64_t my_anc = 0;
-
-  const uint32_t lds_kv = lds_addr(kv_s);
 
   // Per-lane LDS offsets that do not change from tile to tile.
   const int kkey = lane & 31;
@@ -345,7 +401,6 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int vy = (2 * (tg & 1) + ((tj & 3) >> 1)) ^ swz(vkey);
   const int voff_even = vkey * kLatentBytes + (tj & 1) * 8 + (vy << 4);
   const int voff_odd = vkey * kLatentBytes + (tj & 1) * 8 + ((vy ^ 4) << 4);
-  const uint32_t lane16 = lane * 16;
 
   f32x16 o[kColBlocks];
   float m_ref = -INFINITY;  // reference max (log2 units) of this lane's row
@@ -526,15 +581,28 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     for (int w0 = k0; w0 < k1; w0 += kSlotCap) {
       const int wn = min(k1 - w0, kSlotCap);
       const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
-      lds_barrier();  // everyone is done with the previous window or pass
-      for (int i = threadIdx.x; i < ntiles; i += NW * 64) badbits_s[i] = 0u;
+      // The first window of the first pass was requested in the prologue,
+      // together with the query rows; any other is requested once everyone
+      // is done with the previous window or pass.
+      const bool first = kMode == kPassAdaptive && w0 == k0;
+      if (!first) {
+        lds_barrier();
+        request_window(w0, wn);
+      }
+      wait_vmcnt<0>();
       lds_barrier();
+      if (first) {  // the wave's query rows, from its own stage, into registers
+#pragma unroll
+        for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = ld_k(kv_s + wid * kTileBytes, ks);
+      }
+      const int pg0 = w0 >> L.page_shift;
+      const int32_t* ptab = L.page_shift == 0 ? slot_s : pt_s;
       // Physical slot of every key in this window; bad slots are recorded in
       // the tile's bad-key bits and loaded from slot 0 instead.
       int bad = 0;
       for (int i = threadIdx.x; i < wn; i += NW * 64) {
         const int p = w0 + i;
-        const int page = L.page_table[static_cast<size_t>(b) * L.max_pages + (p >> L.page_shift)];
+        const int page = ptab[(p >> L.page_shift) - pg0];
         const int64_t slot = (static_cast<int64_t>(page) << L.page_shift) + (p & ((1 << L.page_shift) - 1));
         const bool ok = page >= 0 && slot < L.num_slots;
         slot_s[i] = ok ? static_cast<int32_t>(slot) : 0;
@@ -548,8 +616,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       if (lane == 0) badw_s[wid] = wave_bad;
       if (kMode == kPassAdaptive && need_mask && w0 == k0 && wid == 0) {
         // sparse decode: every node is a root (one query token per request)
-        const uint64_t a = kSparse ? (lane < T ? 1ull << lane : 0ull)
-                                   : ancestor_bits(L.tree_parent + static_cast<size_t>(b) * T, T, lane, L.err);
+        const uint64_t a = kSparse ? (lane < T ? 1ull << lane : 0ull) : ancestor_bits_of(parent, T, lane, L.err);
         anc_s[lane] = a;
       }
       lds_barrier();
