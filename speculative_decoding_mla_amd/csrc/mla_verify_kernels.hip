@@ -123,6 +123,17 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
                : "memory", "m0");
 }
 
+// 8-byte store at device (agent) scope: written through to the device's point
+// of coherence rather than left dirty in this XCD's L2, so the release at the
+// end of the kernel has nothing to write back and the next kernel, on any
+// XCD, reads the value from the memory-side cache.
+template <typename T>
+__device__ __forceinline__ void store_agent8(T* p, const T& v) {
+  static_assert(sizeof(T) == 8, "8-byte values");
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{}): a
 // loop whose index is a compile-time constant in every copy of the body.
 template <typename F, int... I>
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 
   f32x2* lse_dst = reinterpret_cast<f32x2*>(L.part_lse) + static_cast<size_t>(slot) * L.rows_pad + row;
   if (k0 >= k1) {  // empty split: contributes nothing
-    if (lane < 32) *lse_dst = f32x2{-INFINITY, 0.f};
+    if (lane < 32) store_agent8(lse_dst, f32x2{-INFINITY, 0.f});
     return;
   }
 
@@ -772,7 +783,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     run_pass(PassMode<kPassFixed>{});
   }
 
-  // ---- partial result of this split: O / l in fp16 and lse in log2 units.
+  // ---- partial result of this split: O / l in fp16 and lse in log2 units,
+  // stored at device scope (see store_agent8).
   // O / l is a convex combination of V rows; it is stored as fp16 scaled by
   // 2^-e, with e = 0 unless the row's largest |O / l| reaches 2^15 (then the
   // smallest e that brings it below), and e is kept beside the lse. fp16 adds
@@ -791,7 +803,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   amax = fmaxf(amax, xor32(amax)) * inv;  // the row's 512 values sit on lanes l and l ^ 32
   const int e = max(0, __builtin_amdgcn_frexp_expf(amax) - 15);
   if (lane < 32)
-    *lse_dst = f32x2{l_sum_t > 0.f ? m_ref + __builtin_amdgcn_logf(l_sum_t) : -INFINITY, static_cast<float>(e)};
+    store_agent8(lse_dst, f32x2{l_sum_t > 0.f ? m_ref + __builtin_amdgcn_logf(l_sum_t) : -INFINITY, static_cast<float>(e)});
   if (!row_ok) return;  // padding rows are never read
   const float sc = __builtin_ldexpf(inv, -e);
   f16x4* dst = reinterpret_cast<f16x4*>(L.part_o) + (static_cast<size_t>(slot) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
@@ -800,7 +812,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 v = f32x4{o[cb][4 * q], o[cb][4 * q + 1], o[cb][4 * q + 2], o[cb][4 * q + 3]} * sc;
-      dst[(cb * 4 + q) * 64] = __builtin_convertvector(v, f16x4);
+      store_agent8(&dst[(cb * 4 + q) * 64], __builtin_convertvector(v, f16x4));
       if (q == 3) __builtin_amdgcn_sched_barrier(0);
     }
 }
