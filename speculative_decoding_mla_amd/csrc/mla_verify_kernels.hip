@@ -134,6 +134,15 @@ __device__ __forceinline__ void store_agent8(T* p, const T& v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// v ^ s computed where it is used: as volatile asm it is never hoisted out of
+// a loop, so loop-invariant lane offsets are rebuilt (one VALU operation)
+// instead of held in registers across the tile loop.
+__device__ __forceinline__ uint32_t xor_here(uint32_t v, uint32_t s) {
+  uint32_t r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(v));
+  return r;
+}
+
 // f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{}): a
 // loop whose index is a compile-time constant in every copy of the body.
 template <typename F, int... I>
@@ -664,7 +673,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
         const bool all_latent = NW == 3 ? i < 10 : i < kKeysPerTile / NW;
         if (all_latent) {  // row address in SGPRs, lane offset in a VGPR
           const uint8_t* row = L.kv + static_cast<size_t>(__builtin_amdgcn_readfirstlane(slot)) * L.kv_row_bytes;
-          dma16_sbase(row, lane16 ^ (swz(ins) << 4), stage + ins * kLatentBytes);
+          dma16_sbase(row, xor_here(lane16, swz(ins) << 4), stage + ins * kLatentBytes);
         } else {  // rope parts, or (NW = 3, load 10) either kind: selects, not branches
           const bool latent = ins < kKeysPerTile;
           const int g = ins - kKeysPerTile;
