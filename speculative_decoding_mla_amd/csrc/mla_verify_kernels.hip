@@ -834,9 +834,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 // waves' states are merged the same way in LDS. out = acc / w rounded to bf16
 // once; lse = M + log2 w in natural-log units.
 // A small grid (one request: a few 32-row blocks x 64 fragment slots) takes
-// 16 waves per workgroup to keep enough loads in flight; a large one 8.
+// 16 waves per workgroup to keep enough loads in flight; a large one 8. Four
+// waves per SIMD either way (two 8-wave workgroups per CU).
 template <int kCombineWaves>
-__global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(VerifyLaunch L) {
+__global__ __launch_bounds__(kCombineWaves * 64, 4) void verify_combine_kernel(VerifyLaunch L) {
   __shared__ f32x4 red_acc[kCombineWaves][64];
   __shared__ float red_w[kCombineWaves][64];
   __shared__ float red_m[kCombineWaves][64];
@@ -858,19 +859,47 @@ __global__ __launch_bounds__(kCombineWaves * 64) void verify_combine_kernel(Veri
                     static_cast<size_t>(wb) * 4096 + frag * 64 + lane;
   float mx = -INFINITY, wsum = 0.f;
   f32x4 acc = {};
-#pragma unroll 16
-  for (int s = w; s < count; s += kCombineWaves) {
-    const f32x2 le = pl[static_cast<size_t>(s) * L.rows_pad];
-    const float l2 = le[0];
-    const bool live = row_ok && l2 > -INFINITY;
-    const f32x4 v = row_ok ? __builtin_convertvector(po[s * split_stride], f32x4) : f32x4{};
-    const float nm = live ? fmaxf(mx, l2) : mx;
-    const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - nm);
-    const float wt = live ? __builtin_amdgcn_exp2f(l2 - nm) : 0.f;
-    acc = acc * sc + __builtin_ldexpf(wt, static_cast<int>(le[1])) * (live ? v : f32x4{});
-    wsum = wsum * sc + wt;
-    mx = nm;
-  }
+  // Rounds of R splits per wave: all loads of a round go out before any is
+  // used (indices past the request's last split repeat it and are masked;
+  // padding rows load slots that lie inside the workspace and are discarded
+  // by the select), so a wave waits for one round trip per round, not per
+  // split. R is the wave's share of the splits rounded up to a power of two,
+  // at most 8 (so that four waves fit per SIMD without spills), and few loads
+  // are spent on repeats.
+  auto rounds = [&](auto r_tag) {
+    constexpr int R = decltype(r_tag)::value;
+    for (int s0 = w; s0 < count; s0 += kCombineWaves * R) {
+      f32x2 le[R];
+      f16x4 vh[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int s = min(s0 + i * kCombineWaves, count - 1);
+        le[i] = pl[static_cast<size_t>(s) * L.rows_pad];
+        vh[i] = po[s * split_stride];
+      }
+      // (the values are taken here, unconditionally, so that no load is moved
+      // under the branch of a masked split)
+#pragma unroll
+      for (int i = 0; i < R; ++i) asm volatile("" : "+v"(le[i]), "+v"(vh[i]));
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const f32x4 vi = __builtin_convertvector(vh[i], f32x4);
+        const float l2 = le[i][0];
+        const bool live = s0 + i * kCombineWaves < count && row_ok && l2 > -INFINITY;
+        const float nm = live ? fmaxf(mx, l2) : mx;
+        const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - nm);
+        const float wt = live ? __builtin_amdgcn_exp2f(l2 - nm) : 0.f;
+        acc = acc * sc + __builtin_ldexpf(wt, static_cast<int>(le[i][1])) * (live ? vi : f32x4{});
+        wsum = wsum * sc + wt;
+        mx = nm;
+      }
+    }
+  };
+  const int per_wave = (count + kCombineWaves - 1) / kCombineWaves;
+  if (per_wave > 4) rounds(std::integral_constant<int, 8>{});
+  else if (per_wave > 2) rounds(std::integral_constant<int, 4>{});
+  else if (per_wave > 1) rounds(std::integral_constant<int, 2>{});
+  else rounds(std::integral_constant<int, 1>{});
   red_acc[w][lane] = acc;
   red_w[w][lane] = wsum;
   red_m[w][lane] = mx;
