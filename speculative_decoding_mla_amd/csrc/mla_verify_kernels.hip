@@ -340,39 +340,15 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const bool row_ok = row < L.rows;
 
   // The chain before the first key tile is length -> page table -> keys;
-  // the tree parents (wave 0) and the query rows are requested beside it.
+  // the tree parents (wave 0) are requested with the length, the query rows
+  // (below) right after the page-table entries, so that their loads do not
+  // hold up the length.
   const int n_raw = kSparse ? raw_len(L, b) : L.seq_lens[b];
   int parent = -1;
   if (!kSparse && wid == 0 && lane < T) parent = L.tree_parent[static_cast<size_t>(b) * T + lane];
 
   const uint32_t lds_kv = lds_addr(kv_s);
   const uint32_t lane16 = lane * 16;
-
-  // This wave's 32 query rows go to KV stage `wid` in the layout of a key
-  // tile (row k of the wave in the place of key k), with the same
-  // line-coalesced global->LDS loads; each lane then reads its B operands of
-  // S^T = K Q^T from there exactly as it reads K fragments. (Loaded straight
-  // into registers, every load instruction would gather 32 bytes from each
-  // of 32 rows, and the rows of four waves do not fit the L1: each line came
-  // from L2 four times over.) Padding rows load row 0 of the request; their
-  // results are never stored.
-  {
-    const int r0 = rb * (NW * 32) + wid * 32;  // wave-uniform
-    const uint8_t* qb = reinterpret_cast<const uint8_t*>(L.q) + static_cast<size_t>(b) * L.rows * kRowBytes;
-    const uint32_t stage = lds_kv + wid * kTileBytes;
-#pragma unroll 4
-    for (int k = 0; k < kKeysPerTile; ++k) {
-      const int r = r0 + k < L.rows ? r0 + k : 0;
-      dma16_sbase(qb + static_cast<size_t>(r) * kRowBytes, lane16 ^ (swz(k) << 4), stage + k * kLatentBytes);
-    }
-#pragma unroll
-    for (int g = 0; g < kRopeInstr; ++g) {
-      const int k = 8 * g + (lane >> 3);
-      const int r = r0 + k < L.rows ? r0 + k : 0;
-      dma16(qb + static_cast<size_t>(r) * kRowBytes + ((kVDim / 8 + ((lane & 7) ^ swz(k))) << 4),
-            stage + kRopeBase + g * 1024);
-    }
-  }
 
   const int n = min(max(n_raw, kSparse ? 0 : T), L.capacity);
   if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
@@ -403,6 +379,32 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     for (int i = threadIdx.x; i < ntiles; i += NW * 64) badbits_s[i] = 0u;
   };
   request_window(k0, min(k1 - k0, kSlotCap));
+
+  // This wave's 32 query rows go to KV stage `wid` in the layout of a key
+  // tile (row k of the wave in the place of key k), with the same
+  // line-coalesced global->LDS loads; each lane then reads its B operands of
+  // S^T = K Q^T from there exactly as it reads K fragments. (Loaded straight
+  // into registers, every load instruction would gather 32 bytes from each
+  // of 32 rows, and the rows of four waves do not fit the L1: each line came
+  // from L2 four times over.) Padding rows load row 0 of the request; their
+  // results are never stored.
+  {
+    const int r0 = rb * (NW * 32) + wid * 32;  // wave-uniform
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(L.q) + static_cast<size_t>(b) * L.rows * kRowBytes;
+    const uint32_t stage = lds_kv + wid * kTileBytes;
+#pragma unroll 4
+    for (int k = 0; k < kKeysPerTile; ++k) {
+      const int r = r0 + k < L.rows ? r0 + k : 0;
+      dma16_sbase(qb + static_cast<size_t>(r) * kRowBytes, lane16 ^ (swz(k) << 4), stage + k * kLatentBytes);
+    }
+#pragma unroll
+    for (int g = 0; g < kRopeInstr; ++g) {
+      const int k = 8 * g + (lane >> 3);
+      const int r = r0 + k < L.rows ? r0 + k : 0;
+      dma16(qb + static_cast<size_t>(r) * kRowBytes + ((kVDim / 8 + ((lane & 7) ^ swz(k))) << 4),
+            stage + kRopeBase + g * 1024);
+    }
+  }
 
   bf16x8 qf[kQSteps];  // lane: dims 16ks + 8*hsel + 0..7 of row lane%32
   const int node = row_ok ? row / L.heads : 0;
