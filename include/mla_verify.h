@@ -97,7 +97,7 @@ typedef struct {
 
 /* Bytes of workspace mla_verify_attention needs for this descriptor: a 256-byte
  * header whose first 4 bytes are the device error word, then per-split partial
- * outputs (fp32) and partial log-sum-exps. Returns 0 for a descriptor that
+ * log-sum-exps and partial outputs (fp16). Returns 0 for a descriptor that
  * mla_verify_attention would reject. */
 MLA_API size_t mla_verify_workspace_bytes(const mla_verify_desc* d);
 

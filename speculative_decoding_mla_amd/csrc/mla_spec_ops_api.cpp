@@ -82,6 +82,7 @@ mla_status mla_sparse_decode(const mla_sparse_desc* d, const void* q, const void
   L.capacity = d->topk;
   L.min_len = 0;
   L.quiet_unused = 1;
+  L.col_parts = mlav::col_parts_for(d->batch, d->nsplit, rp.row_blocks);
   L.scale_log2 = d->sm_scale * 1.4426950408889634f;
   if (mlav::launch_partial(L, stream) != hipSuccess) return MLA_ERR_HIP;
   return launched(mlav::launch_combine(L, stream));

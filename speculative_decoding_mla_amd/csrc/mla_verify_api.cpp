@@ -115,6 +115,7 @@ mla_status prepare(const mla_verify_desc* d, const void* q, const void* kv_cache
   L->capacity = static_cast<int32_t>(static_cast<int64_t>(d->max_pages) * d->page_size);
   L->min_len = d->num_nodes;
   L->quiet_unused = 0;
+  L->col_parts = mlav::col_parts_for(d->batch, d->nsplit, rp.row_blocks);
   L->scale_log2 = d->sm_scale * 1.4426950408889634f;
   return MLA_OK;
 }

@@ -9,6 +9,8 @@ namespace mlav {
 constexpr int kQkDim = 576;       // 512 latent + 64 rope
 constexpr int kVDim = 512;        // V = leading 512 entries of the latent row
 constexpr int kMaxNodes = 64;     // ancestor sets are 64-bit masks
+constexpr int kCusPerDevice = 256;  // MI355X
+constexpr int kMaxColParts = 4;     // partial-lse records per (split, row): one per column part
 constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block of (node, head) rows per wave
 constexpr int kHeaderBytes = 256; // workspace header; word 0 is the device error word
 
@@ -22,7 +24,7 @@ struct VerifyLaunch {
   uint16_t* out;               // bf16 [B, T, H, 512]
   float* lse;                  // [B, T, H]
   uint32_t* err;               // device error word (workspace head)
-  float* part_lse;             // [B*nsplit slots][rows_pad] pairs {partial lse (log2 units), scale exponent}
+  float* part_lse;             // [B*nsplit slots][rows_pad][kMaxColParts] pairs {partial lse (log2 units), scale exponent}
   uint16_t* part_o;            // fragment-ordered partial outputs, fp16, scaled by 2^-exponent
   int64_t kv_row_bytes;        // bytes between kv rows
   int64_t num_slots;
@@ -31,6 +33,7 @@ struct VerifyLaunch {
   int32_t capacity;            // max_pages * page_size (clamp bound for seq_lens)
   int32_t min_len;             // lower clamp bound for seq_lens: T (verify) or 0 (sparse decode)
   int32_t quiet_unused;        // 1: a page id of -1 is an unused entry, masked without an error bit
+  int32_t col_parts;           // 1, 2 or 4 workgroups per (split, row block), each over 512/col_parts columns
   float scale_log2;            // sm_scale * log2(e)
 };
 
@@ -39,6 +42,8 @@ struct RowPlan {
   int rows, waves_per_wg, row_blocks, rows_pad;
 };
 RowPlan plan_rows(int nodes, int heads);
+// Column parts for a grid of batch * nsplit * row_blocks workgroups.
+int col_parts_for(int batch, int nsplit, int row_blocks);
 
 size_t workspace_bytes(int batch, int nsplit, int rows_pad);
 size_t part_lse_offset();

@@ -303,8 +303,13 @@ constexpr int kPassFixed = 2;     // accumulate against a given reference
 // kSparse: one query token per request over an index list (sparse top-k
 // decode): lengths may be absent, an entry of -1 is unused, every node is a
 // root. A compile-time switch, so the verify instantiations carry none of it.
-template <int NW, bool kSparse>
+// NCP: column parts. With NCP > 1, NCP workgroups share a (split, row block):
+// each computes the same scores and weights but only its 512/NCP output
+// columns (kCB column blocks), so a grid that would leave CUs idle spreads the
+// PV products, the normalisation and the partial stores over NCP CUs.
+template <int NW, bool kSparse, int NCP>
 __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch L) {
+  constexpr int kCB = kColBlocks / NCP;
   constexpr int kInstrPerWave = kTileInstr / NW;
   static_assert(kTileInstr % NW == 0, "tile loads must split evenly over the waves");
   constexpr int kTilesPerWindow = kSlotCap / kKeysPerTile;
@@ -322,11 +327,14 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int hsel = lane >> 5;
 
   // XCD-aware order: workgroup i runs on XCD i % 8, so consecutive logical ids
-  // (the row blocks of one split) are placed on one XCD in dispatch order.
-  const int total = L.batch * L.nsplit * L.row_blocks;
+  // (the column parts and row blocks of one split) are placed on one XCD in
+  // dispatch order and share its L2 for the key rows.
+  const int total = L.batch * L.nsplit * L.row_blocks * NCP;
   const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (logical >= total) return;
+  const int logical_cp = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical_cp >= total) return;
+  const int cp = logical_cp % NCP;  // column part: blocks cp*kCB .. cp*kCB + kCB - 1
+  const int logical = logical_cp / NCP;
   const int rb = logical % L.row_blocks;
   const int slot = logical / L.row_blocks;  // split slot in [0, B*NSPLIT)
   const SplitRange sr = split_plan(L, slot, true, lane);
@@ -357,7 +365,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int k0 = s * chunk;
   const int k1 = min(n, k0 + chunk);
 
-  f32x2* lse_dst = reinterpret_cast<f32x2*>(L.part_lse) + static_cast<size_t>(slot) * L.rows_pad + row;
+  f32x2* lse_dst =
+      reinterpret_cast<f32x2*>(L.part_lse) + (static_cast<size_t>(slot) * L.rows_pad + row) * kMaxColParts + cp;
   if (k0 >= k1) {  // empty split: contributes nothing
     if (lane < 32) store_agent8(lse_dst, f32x2{-INFINITY, 0.f});
     return;
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int voff_even = vkey * kLatentBytes + (tj & 1) * 8 + (vy << 4);
   const int voff_odd = vkey * kLatentBytes + (tj & 1) * 8 + ((vy ^ 4) << 4);
 
-  f32x16 o[kColBlocks];
+  f32x16 o[kCB];
   float m_ref = -INFINITY;  // reference max (log2 units) of this lane's row
   float m_max = -INFINITY;  // exact row max (pass B)
   float l_sum = 0.f;        // sum of fp32 weights (this lane's half of the keys)
@@ -559,29 +568,31 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     for (int piece = 0; piece < 19; ++piece) softmax_piece(mode_tag, piece, sm, tsc, pf);
   };
 
-  // V^T fragment of PV step i (column block i%16, keys 16*(i/16)..+15).
+  // V^T fragment of PV step i (column block cp*kCB + i%kCB, keys
+  // 16*(i/kCB)..+15); kCB is even, so the block's parity is i's.
   auto ld_v = [&](const uint8_t* st, int i, i16x4 (&v)[2]) {
-    const int cb = i % kColBlocks, kk = i / kColBlocks;
-    const uint8_t* vb = st + (cb & 1 ? voff_odd : voff_even) + (cb >> 1) * 128;
+    const int cb = i % kCB, kk = i / kCB;
+    const uint8_t* vb = st + cp * (kCB / 2) * 128 + (cb & 1 ? voff_odd : voff_even) + (cb >> 1) * 128;
     v[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk) * kLatentBytes));
     v[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vb + (16 * kk + 8) * kLatentBytes));
   };
-  // O^T += V^T P^T: 32 MFMA steps into the AGPR-resident accumulator, V^T
-  // reads three steps ahead. Keys 0-15 of the tile go into all 16 column
+  // O^T += V^T P^T: 2*kCB MFMA steps into the AGPR-resident accumulator, V^T
+  // reads three steps ahead. Keys 0-15 of the tile go into all kCB column
   // blocks before keys 16-31, so no MFMA waits for the one before it (a
-  // dependent MFMA issues only after its predecessor has finished). Issued as inline asm so that the order of loads,
-  // MFMAs and the interleaved VALU work (between(i) after step i) is kept.
+  // dependent MFMA issues only after its predecessor has finished). Issued as
+  // inline asm so that the order of loads, MFMAs and the interleaved VALU work
+  // (between(i) after step i) is kept.
   auto pv = [&](const uint8_t* st, const bf16x8 (&pf)[2], auto&& between) {
     i16x4 vr[4][2];
 #pragma unroll
     for (int i = 0; i < 3; ++i) ld_v(st, i, vr[i]);
 #pragma unroll
-    for (int i = 0; i < 2 * kColBlocks; ++i) {
-      if (i + 3 < 2 * kColBlocks) ld_v(st, i + 3, vr[(i + 3) & 3]);
+    for (int i = 0; i < 2 * kCB; ++i) {
+      if (i + 3 < 2 * kCB) ld_v(st, i + 3, vr[(i + 3) & 3]);
       const i16x8 v = __builtin_shufflevector(vr[i & 3][0], vr[i & 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                   : "+a"(o[i % kColBlocks])
-                   : "v"(__builtin_bit_cast(bf16x8, v)), "v"(pf[i / kColBlocks]));
+                   : "+a"(o[i % kCB])
+                   : "v"(__builtin_bit_cast(bf16x8, v)), "v"(pf[i / kCB]));
       between(i);
     }
   };
@@ -596,7 +607,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     constexpr bool kAccum = kMode != kPassMaxOnly;
     if constexpr (kAccum) {
 #pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb) o[cb] = f32x16{};
+      for (int cb = 0; cb < kCB; ++cb) o[cb] = f32x16{};
       l_sum = 0.f;
       l_pb = 0.f;
     }
@@ -755,10 +766,16 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
           // phase 2: PV(t) on the matrix cores; the masking of tile t+1's
           // scores (one element per step) on the VALU in between.
           const uint32_t vsh = visible_bits(w0, wn, t + 1) >> (4 * hsel);
+          // (16 elements over 2*kCB steps: one per step, or 16/(2*kCB))
+          constexpr int kMaskPer = 2 * kCB >= 16 ? 1 : 16 / (2 * kCB);
           auto mask_step = [&](int i) {
-            if (i < 16) {
-              tsc[i] = ((vsh >> (8 * (i >> 2) + (i & 3))) & 1u) ? acc[i] * L.scale_log2 : -INFINITY;
-              asm volatile("" : "+v"(tsc[i]));
+#pragma unroll
+            for (int k = 0; k < kMaskPer; ++k) {
+              const int m = i * kMaskPer + k;
+              if (m < 16) {
+                tsc[m] = ((vsh >> (8 * (m >> 2) + (m & 3))) & 1u) ? acc[m] * L.scale_log2 : -INFINITY;
+                asm volatile("" : "+v"(tsc[m]));
+              }
             }
           };
           if constexpr (kAccum) {
@@ -797,10 +814,11 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   // ---- partial result of this split: O / l in fp16 and lse in log2 units,
   // stored at device scope (see store_agent8).
   // O / l is a convex combination of V rows; it is stored as fp16 scaled by
-  // 2^-e, with e = 0 unless the row's largest |O / l| reaches 2^15 (then the
-  // smallest e that brings it below), and e is kept beside the lse. fp16 adds
-  // at most 2^-12 relative to each stored value, well inside one bf16 rounding
-  // of the final output.
+  // 2^-e, with e = 0 unless the largest |O / l| of the row's columns in this
+  // part reaches 2^15 (then the smallest e that brings it below), and e is
+  // kept beside the lse in the part's own record. fp16 adds at most 2^-12
+  // relative to each stored value, well inside one bf16 rounding of the final
+  // output.
   // (wait states between the last XDL write of O and the reads below)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
   const float l_sum_t = l_sum + __shfl_xor(l_sum, 32);
@@ -808,10 +826,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const float inv = l_pb_t > 0.f ? 1.f / l_pb_t : 0.f;
   float amax = 0.f;
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb)
+  for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(o[cb][j]));
-  amax = fmaxf(amax, xor32(amax)) * inv;  // the row's 512 values sit on lanes l and l ^ 32
+  amax = fmaxf(amax, xor32(amax)) * inv;  // the row's values sit on lanes l and l ^ 32
   const int e = max(0, __builtin_amdgcn_frexp_expf(amax) - 15);
   if (lane < 32)
     store_agent8(lse_dst, f32x2{l_sum_t > 0.f ? m_ref + __builtin_amdgcn_logf(l_sum_t) : -INFINITY, static_cast<float>(e)});
@@ -819,11 +837,11 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const float sc = __builtin_ldexpf(inv, -e);
   f16x4* dst = reinterpret_cast<f16x4*>(L.part_o) + (static_cast<size_t>(slot) * (L.rows_pad / 32) + row / 32) * 4096 + lane;
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb)
+  for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 v = f32x4{o[cb][4 * q], o[cb][4 * q + 1], o[cb][4 * q + 2], o[cb][4 * q + 3]} * sc;
-      store_agent8(&dst[(cb * 4 + q) * 64], __builtin_convertvector(v, f16x4));
+      store_agent8(&dst[((cp * kCB + cb) * 4 + q) * 64], __builtin_convertvector(v, f16x4));
       if (q == 3) __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -855,7 +873,10 @@ __global__ __launch_bounds__(kCombineWaves * 64, 4) void verify_combine_kernel(V
   const SplitRange sr = split_plan(L, b, false, lane);  // this request's split slots
   const int first = __builtin_amdgcn_readfirstlane(sr.first);
   const int count = __builtin_amdgcn_readfirstlane(sr.count);
-  const f32x2* pl = reinterpret_cast<const f32x2*>(L.part_lse) + static_cast<size_t>(first) * L.rows_pad + row;
+  // the record {lse, e} of the column part that wrote this fragment
+  const int part = (frag >> 2) * L.col_parts / kColBlocks;
+  const f32x2* pl =
+      reinterpret_cast<const f32x2*>(L.part_lse) + (static_cast<size_t>(first) * L.rows_pad + row) * kMaxColParts + part;
   const size_t split_stride = static_cast<size_t>(nwb) * 4096;
   const f16x4* po = reinterpret_cast<const f16x4*>(L.part_o) + static_cast<size_t>(first) * split_stride +
                     static_cast<size_t>(wb) * 4096 + frag * 64 + lane;
@@ -876,7 +897,7 @@ __global__ __launch_bounds__(kCombineWaves * 64, 4) void verify_combine_kernel(V
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int s = min(s0 + i * kCombineWaves, count - 1);
-        le[i] = pl[static_cast<size_t>(s) * L.rows_pad];
+        le[i] = pl[static_cast<size_t>(s) * L.rows_pad * kMaxColParts];
         vh[i] = po[s * split_stride];
       }
       // (the values are taken here, unconditionally, so that no load is moved
@@ -947,7 +968,7 @@ RowPlan plan_rows(int nodes, int heads) {
 size_t part_lse_offset() { return kHeaderBytes; }
 
 size_t part_o_offset(int batch, int nsplit, int rows_pad) {
-  const size_t lse_bytes = static_cast<size_t>(batch) * nsplit * rows_pad * 2 * sizeof(float);
+  const size_t lse_bytes = static_cast<size_t>(batch) * nsplit * rows_pad * kMaxColParts * 2 * sizeof(float);
   return (part_lse_offset() + lse_bytes + 255) & ~static_cast<size_t>(255);
 }
 
@@ -962,23 +983,40 @@ hipError_t launch_tree_mask(const int32_t* tree_parent, uint64_t* anc, int batch
   return hipGetLastError();
 }
 
-template <bool kSparse>
+template <bool kSparse, int NCP>
 void launch_partial_t(const VerifyLaunch& L, hipStream_t stream) {
-  const int total = L.batch * L.nsplit * L.row_blocks;
+  const int total = L.batch * L.nsplit * L.row_blocks * NCP;
   const int grid = (total + 7) / 8 * 8;
   switch (L.waves_per_wg) {
-    case 1: hipLaunchKernelGGL((verify_partial_kernel<1, kSparse>), dim3(grid), dim3(64), 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((verify_partial_kernel<2, kSparse>), dim3(grid), dim3(128), 0, stream, L); break;
-    case 3: hipLaunchKernelGGL((verify_partial_kernel<3, kSparse>), dim3(grid), dim3(192), 0, stream, L); break;
-    default: hipLaunchKernelGGL((verify_partial_kernel<4, kSparse>), dim3(grid), dim3(256), 0, stream, L); break;
+    case 1: hipLaunchKernelGGL((verify_partial_kernel<1, kSparse, NCP>), dim3(grid), dim3(64), 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((verify_partial_kernel<2, kSparse, NCP>), dim3(grid), dim3(128), 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((verify_partial_kernel<3, kSparse, NCP>), dim3(grid), dim3(192), 0, stream, L); break;
+    default: hipLaunchKernelGGL((verify_partial_kernel<4, kSparse, NCP>), dim3(grid), dim3(256), 0, stream, L); break;
   }
+}
+
+template <bool kSparse>
+void launch_partial_s(const VerifyLaunch& L, hipStream_t stream) {
+  if (L.col_parts == 4)
+    launch_partial_t<kSparse, 4>(L, stream);
+  else if (L.col_parts == 2)
+    launch_partial_t<kSparse, 2>(L, stream);
+  else
+    launch_partial_t<kSparse, 1>(L, stream);
+}
+
+int col_parts_for(int batch, int nsplit, int row_blocks) {
+  // Column parts while the (split, row block) workgroups would fill at most a
+  // quarter (4 parts) or half (2 parts) of the CUs.
+  const int64_t wgs = static_cast<int64_t>(batch) * nsplit * row_blocks;
+  return wgs * 4 <= kCusPerDevice ? 4 : (wgs * 2 <= kCusPerDevice ? 2 : 1);
 }
 
 hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream) {
   if (L.quiet_unused)
-    launch_partial_t<true>(L, stream);
+    launch_partial_s<true>(L, stream);
   else
-    launch_partial_t<false>(L, stream);
+    launch_partial_s<false>(L, stream);
   return hipGetLastError();
 }
 

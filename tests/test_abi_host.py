@@ -51,21 +51,22 @@ def _desc(**kw):
 
 
 def test_workspace_formula():
-    # Header 256 B; per split slot and padded row a pair of floats {lse, scale
-    # exponent}; then the fp16 partial outputs (512 per padded row), 256-B aligned.
+    # Header 256 B; per split slot, padded row and column part (4) a pair of
+    # floats {lse, scale exponent}; then the fp16 partial outputs (512 per padded
+    # row), 256-B aligned.
     # 16 nodes x 8 heads = 128 rows = 4 waves of 32 in one row block.
     d = _desc()
     rows_pad, b, s = 128, 2, 64
-    lse_bytes = b * s * rows_pad * 8
+    lse_bytes = b * s * rows_pad * 4 * 8
     o_off = (256 + lse_bytes + 255) // 256 * 256
     assert bd.workspace_bytes(d) == o_off + b * s * rows_pad * 512 * 2
     # 9 nodes x 8 heads = 72 rows -> 3 waves (96 padded rows)
     d = _desc(num_nodes=9, batch=1, nsplit=3)
-    lse_bytes = 1 * 3 * 96 * 8
+    lse_bytes = 1 * 3 * 96 * 4 * 8
     assert bd.workspace_bytes(d) == (256 + lse_bytes + 255) // 256 * 256 + 3 * 96 * 512 * 2
     # 32 nodes x 8 heads = 256 rows -> two row blocks of 128
     d = _desc(num_nodes=32, batch=1, nsplit=1)
-    assert bd.workspace_bytes(d) == (256 + 256 * 8 + 255) // 256 * 256 + 256 * 512 * 2
+    assert bd.workspace_bytes(d) == (256 + 256 * 4 * 8 + 255) // 256 * 256 + 256 * 512 * 2
 
 @pytest.mark.parametrize("kw,status", [
     (dict(num_nodes=0), -2), (dict(num_nodes=65), -2), (dict(batch=0), -2), (dict(num_heads=0), -2),
