@@ -24,7 +24,7 @@ struct VerifyLaunch {
   uint16_t* out;               // bf16 [B, T, H, 512]
   float* lse;                  // [B, T, H]
   uint32_t* err;               // device error word (workspace head)
-  float* part_lse;             // [B*nsplit slots][rows_pad][kMaxColParts] pairs {partial lse (log2 units), scale exponent}
+  float* part_lse;             // [B*nsplit slots][kMaxColParts][rows_pad] pairs {partial lse (log2 units), scale exponent}
   uint16_t* part_o;            // fragment-ordered partial outputs, fp16, scaled by 2^-exponent
   int64_t kv_row_bytes;        // bytes between kv rows
   int64_t num_slots;

@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   const int k1 = min(n, k0 + chunk);
 
   f32x2* lse_dst =
-      reinterpret_cast<f32x2*>(L.part_lse) + (static_cast<size_t>(slot) * L.rows_pad + row) * kMaxColParts + cp;
+      reinterpret_cast<f32x2*>(L.part_lse) + (static_cast<size_t>(slot) * kMaxColParts + cp) * L.rows_pad + row;
   if (k0 >= k1) {  // empty split: contributes nothing
     if (lane < 32) store_agent8(lse_dst, f32x2{-INFINITY, 0.f});
     return;
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(kCombineWaves * 64, 4) void verify_combine_kernel(V
   // the record {lse, e} of the column part that wrote this fragment
   const int part = (frag >> 2) * L.col_parts / kColBlocks;
   const f32x2* pl =
-      reinterpret_cast<const f32x2*>(L.part_lse) + (static_cast<size_t>(first) * L.rows_pad + row) * kMaxColParts + part;
+      reinterpret_cast<const f32x2*>(L.part_lse) + (static_cast<size_t>(first) * kMaxColParts + part) * L.rows_pad + row;
   const size_t split_stride = static_cast<size_t>(nwb) * 4096;
   const f16x4* po = reinterpret_cast<const f16x4*>(L.part_o) + static_cast<size_t>(first) * split_stride +
                     static_cast<size_t>(wb) * 4096 + frag * 64 + lane;
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(kCombineWaves * 64, 4) void verify_combine_kernel(V
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int s = min(s0 + i * kCombineWaves, count - 1);
-        le[i] = pl[static_cast<size_t>(s) * L.rows_pad * kMaxColParts];
+        le[i] = pl[static_cast<size_t>(s) * kMaxColParts * L.rows_pad];
         vh[i] = po[s * split_stride];
       }
       // (the values are taken here, unconditionally, so that no load is moved

@@ -120,6 +120,9 @@ def test_parity_tiny_config(nsplit):
 
 
 def test_parity_4k_config_nsplit_sweep():
+    # One request of 128 rows (one row block): NSPLIT 64, 1 and 7 give grids of
+    # at most a quarter of the CUs (four column parts), 128 half of them (two),
+    # 257 more (one), so every column-part mode meets the oracle here.
     case = make_case("C2")
     ref = oracle_case(case)
     dc = device_case(case)
