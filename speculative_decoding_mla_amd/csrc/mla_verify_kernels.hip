@@ -537,8 +537,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       const float p1 = __builtin_amdgcn_exp2f(tsc[2 * k + 1] - sm.mu);
       sm.ts += p0 + p1;
       sm.pb2[k] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-      const f32x2 back = __builtin_convertvector(sm.pb2[k], f32x2);
-      sm.tb += back[0] + back[1];
+      // the rounded pair summed in one bf16 dot product with (1, 1)
+      sm.tb = __builtin_amdgcn_fdot2_f32_bf16(sm.pb2[k], bf16x2{static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)},
+                                              sm.tb, false);
     } else if (kMode != kPassMaxOnly && piece == 18) {
       l_sum += sm.ts;
       l_pb += sm.tb;
