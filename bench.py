@@ -265,13 +265,15 @@ def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, st
                                          ws)
 
     R = rep.replicas
-    per_graph = min(R, steps)
-    g_full = capture(torch, [full_call(r) for r in range(per_graph)])
+    # At least 64 calls per graph (cycling over the replicas), so that a small
+    # R does not add a graph launch per call.
+    per_graph = min(max(R, 64), steps)
+    g_full = capture(torch, [full_call(r % R) for r in range(per_graph)])
     rem = steps % per_graph
-    g_rem = capture(torch, [full_call(r) for r in range(rem)]) if rem else None
+    g_rem = capture(torch, [full_call(r % R) for r in range(rem)]) if rem else None
     # warmup: W untimed steps
-    w_graph = min(R, max(warmup, 1))
-    g_w = capture(torch, [full_call(r) for r in range(w_graph)])
+    w_graph = min(max(R, 64), max(warmup, 1))
+    g_w = capture(torch, [full_call(r % R) for r in range(w_graph)])
     for _ in range(max(1, warmup // w_graph)):
         g_w.replay()
     torch.cuda.synchronize()
@@ -284,10 +286,11 @@ def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, st
     ms_per_step = t0.elapsed_time(t1) / steps
 
     # the dominant kernel alone, timed with events on the stream it runs on
-    g_p = capture(torch, [partial_call(r) for r in range(R)])
+    n_p = max(R, 64)
+    g_p = capture(torch, [partial_call(r % R) for r in range(n_p)])
     g_p.replay()
     torch.cuda.synchronize()
-    reps = max(1, min(50, (steps + R - 1) // R))
+    reps = max(1, min(50, (steps + n_p - 1) // n_p))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -295,7 +298,7 @@ def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, st
         g_p.replay()
     e1.record()
     torch.cuda.synchronize()
-    partial_us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+    partial_us = e0.elapsed_time(e1) * 1e3 / (reps * n_p)
     # leave the full result of replica 0 in out/lse
     full_call(0)()
     torch.cuda.synchronize()
@@ -323,6 +326,26 @@ def cpu_baseline(case, budget_s=10.0, max_reps=20):
             break
     med = statistics.median(times)
     return med, len(times), threads, ref
+
+
+def cpu_baseline_one_thread(case, budget_s=10.0, max_reps=5):
+    """The same oracle timing with the BLAS pool limited to one thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        med, reps, _, _ = cpu_baseline(case, budget_s=budget_s, max_reps=max_reps)
+    return med, reps
+
+
+def measured_peaks():
+    """The achievable peaks of this GPU, measured in this run by the mla_peaks
+    program (streaming read, copy, bf16 MFMA), as a child process."""
+    import subprocess
+    exe = os.path.join(ROOT, "speculative_decoding_mla_amd", "lib", "mla_peaks")
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (OSError, ValueError, IndexError, subprocess.TimeoutExpired):
+        return None
 
 
 def cpu_model():
@@ -557,12 +580,13 @@ def measure_next_rows(torch, mv, with_cpu=True, only=None):
 
 # ---------------------------------------------------------------- main
 
-def measure_case(torch, mv, case, nsplit, steps, warmup, seed):
+def measure_case(torch, mv, case, nsplit, steps, warmup, seed, replicas=None):
     rows = logical_rows_of_case(case)
     lr = bf16_from_bits(torch, rows).cuda()
     q = bf16_from_bits(torch, case.q).cuda()
     kvb = kv_bytes(case.seq_lens)
-    replicas = max(1, math.ceil(ROTATE_BYTES / max(kvb, 1)))
+    if replicas is None:
+        replicas = max(1, math.ceil(ROTATE_BYTES / max(kvb, 1)))
     rep = Replicated(torch, lr, q, case.seq_lens, case.tree_parent, case.page_size, replicas, seed,
                      layout=case_layout(case))
     del lr
@@ -693,12 +717,35 @@ def main():
                 roofline=roof, device_error=dev_err)
 
     log(f"{args.workload}: {lat_us:.2f} us/step, partial kernel {partial_us:.2f} us")
+    # The same workload from one replica: its KV stays in the 256 MB Infinity
+    # Cache between steps. Reported beside the rotating-replica number, which
+    # is the measurement; this one is labelled cache-resident.
+    (w_ms, w_partial_us, *_), w_rep = measure_case(torch, mv, case, nsplit, 512, 64, args.seed, replicas=1)
+    del w_rep
+    torch.cuda.empty_cache()
+    line["warm_cache_resident"] = dict(latency_us=round(w_ms * 1e3, 3), partial_us=round(w_partial_us, 3),
+                                       eff_kv_gbs=round(effective_kv_gbs(case.seq_lens, w_ms * 1e-3), 1),
+                                       note="one replica, KV resident in the Infinity Cache across steps")
+    peaks = measured_peaks()
+    if peaks:
+        line["measured_peaks"] = dict(hbm_read_gbs=peaks.get("hbm_read_gbs"),
+                                      mfma_bf16_tflops=peaks.get("mfma_bf16_tflops"),
+                                      source="mla_peaks, run by this benchmark on this GPU")
+        den = peaks.get("hbm_read_gbs") if roof["bound"] == "hbm" else peaks.get("mfma_bf16_tflops")
+        if den:
+            roof["frac_of_measured_peak"] = round(roof["achieved"] / den, 4)
+        if peaks.get("hbm_read_gbs"):
+            line["eff_kv_frac_of_measured_read"] = round(eff / peaks["hbm_read_gbs"], 4)
     if not args.no_cpu:
         log("timing the CPU oracle")
         med, reps, threads, ref = cpu_baseline(case)
         line["cpu_baseline"] = dict(value=round(kvb / med / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
                                     sample=f"whole {args.workload} verify call, {reps} timed runs, median "
                                            f"{med * 1e6:.0f} us; CPU {cpu_model()}")
+        med1, reps1 = cpu_baseline_one_thread(case)
+        line["cpu_baseline_1thread"] = dict(value=round(kvb / med1 / 1e9, 4), unit="GB/s", cores=1,
+                                            kind="oracle", sample=f"the same call, {reps1} timed runs, median "
+                                                                  f"{med1 * 1e6:.0f} us, BLAS limited to 1 thread")
         from oracle import bf16_bits_to_f64
         o = bf16_bits_to_f64(gpu_out)
         line["parity_vs_oracle"] = dict(out_max_abs=float(np.abs(o - ref[0]).max()),
