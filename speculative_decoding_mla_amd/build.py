@@ -57,15 +57,25 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950: the shared library and the peak
-    microbenchmark executable. Always recompiles. Returns the library path."""
+    microbenchmark executable. Always recompiles (the translation units in
+    parallel, then one link). Returns the library path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(LIB_DIR, exist_ok=True)
+    obj_dir = os.path.join(LIB_DIR, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, s + ".o") for s in SOURCES]
+    peaks_tmp = PEAKS_PATH + ".tmp"
+    jobs = [[hipcc(), *HIP_FLAGS, "-c", "-x", "hip", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+    jobs.append([hipcc(), *[f for f in HIP_FLAGS if f != "-fvisibility=hidden"], "-o", peaks_tmp,
+                 os.path.join(CSRC, "mla_peaks.hip")])
+    with ThreadPoolExecutor(max_workers=len(jobs)) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
     tmp = LIB_PATH + ".tmp"
-    _run([hipcc(), *HIP_FLAGS, "-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES], verbose)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
-    tmp = PEAKS_PATH + ".tmp"
-    _run([hipcc(), *[f for f in HIP_FLAGS if f != "-fvisibility=hidden"], "-o", tmp,
-          os.path.join(CSRC, "mla_peaks.hip")], verbose)
-    os.replace(tmp, PEAKS_PATH)
+    os.replace(peaks_tmp, PEAKS_PATH)
     return LIB_PATH
 
 
