@@ -769,21 +769,34 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
           const uint32_t vsh = visible_bits(w0, wn, t + 1) >> (4 * hsel);
           // (16 elements over 2*kCB steps: one per step, or 16/(2*kCB))
           constexpr int kMaskPer = 2 * kCB >= 16 ? 1 : 16 / (2 * kCB);
-          auto mask_step = [&](int i) {
+          // Scale on the VALU between the MFMAs; the mask after them, and only
+          // for a tile that is not wholly visible (tree keys, the end of the
+          // window, bad slots): a tile of context keys needs none.
+          auto scale_step = [&](int i) {
 #pragma unroll
             for (int k = 0; k < kMaskPer; ++k) {
               const int m = i * kMaskPer + k;
               if (m < 16) {
-                tsc[m] = ((vsh >> (8 * (m >> 2) + (m & 3))) & 1u) ? acc[m] * L.scale_log2 : -INFINITY;
+                tsc[m] = acc[m] * L.scale_log2;
                 asm volatile("" : "+v"(tsc[m]));
               }
             }
           };
           if constexpr (kAccum) {
-            pv(st, pf, mask_step);
+            pv(st, pf, scale_step);
           } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mask_step(i);
+            for (int i = 0; i < 16; ++i) scale_step(i);
+          }
+          const int tk1 = (t + 1) * kKeysPerTile;
+          const bool all_visible = w0 + tk1 + kKeysPerTile <= ctx && wn - tk1 >= kKeysPerTile &&
+                                   __builtin_amdgcn_readfirstlane(badbits_s[t + 1]) == 0u;
+          if (!all_visible) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+              tsc[m] = ((vsh >> (8 * (m >> 2) + (m & 3))) & 1u) ? tsc[m] : -INFINITY;
+              asm volatile("" : "+v"(tsc[m]));  // (keeps the branch: no speculative selects)
+            }
           }
         }
       };
