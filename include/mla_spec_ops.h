@@ -139,6 +139,30 @@ MLA_API mla_status mla_commit_accepted(int32_t* page_table, int32_t max_pages, c
                                        void* kv_cache, int64_t num_kv_slots, int64_t kv_row_stride,
                                        const int32_t* dest_slots, uint32_t* dev_err, hipStream_t stream);
 
+/* ------------------------------------------------------------------ accept and commit in one launch
+ * mla_tree_accept followed by mla_commit_accepted (the verify-kernel page,
+ * Part II and Part IV for the accept, Part VI and Part VIII for the commit),
+ * one workgroup per request: the accept's outputs are written exactly as
+ * mla_tree_accept writes them, and the commit takes the path from on-chip
+ * memory rather than reading accept_len / accept_path back. The results equal
+ * those of the two calls in sequence.
+ *   tree_parent, draft_tokens, target_tokens, accept_len, accept_path,
+ *   commit_tokens: as for mla_tree_accept (accept_len and accept_path are
+ *                  written; commit_tokens nullable).
+ *   page_table, max_pages, seq_lens, context_lens, freed_slots, kv_cache,
+ *   num_kv_slots, kv_row_stride, dest_slots: as for mla_commit_accepted.
+ *   dev_err:       nullable; MLA_DEVERR_BAD_PARENT as for mla_tree_accept,
+ *                  MLA_DEVERR_INDEX_RANGE for a seq_len outside [T, max_pages]
+ *                  (clamped), MLA_DEVERR_SLOT_RANGE as for mla_commit_accepted.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ALIGN, MLA_ERR_HIP. */
+MLA_API mla_status mla_accept_commit(const int32_t* tree_parent, const int32_t* draft_tokens,
+                                     const int32_t* target_tokens, int32_t batch, int32_t num_nodes,
+                                     int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                                     int32_t* accept_len, int32_t* accept_path, int32_t* commit_tokens,
+                                     int32_t* context_lens, int32_t* freed_slots, void* kv_cache,
+                                     int64_t num_kv_slots, int64_t kv_row_stride, const int32_t* dest_slots,
+                                     uint32_t* dev_err, hipStream_t stream);
+
 /* ------------------------------------------------------------------ sliding-window gather
  * Page "One Blocking Memcpy Per Verify Step", section "The sync, and the bound
  * that replaced it": a draft model keeps the most recent W tokens in a cache

@@ -121,6 +121,9 @@ def load_library():
         lib.mla_tree_accept.restype = ctypes.c_int
         lib.mla_commit_accepted.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp]
         lib.mla_commit_accepted.restype = ctypes.c_int
+        lib.mla_accept_commit.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
+                                          vp, vp]
+        lib.mla_accept_commit.restype = ctypes.c_int
         lib.mla_window_map.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp]
         lib.mla_window_map.restype = ctypes.c_int
         lib.mla_indexer_logits.argtypes = [ctypes.POINTER(MlaIndexerDesc), vp, vp, vp, vp, vp, vp, vp, vp]
@@ -368,6 +371,35 @@ def commit_accepted(page_table: torch.Tensor, seq_lens: torch.Tensor, num_nodes:
         _ptr(page_table), max_pages, _ptr(seq_lens), b, num_nodes, _ptr(accept_len), _ptr(accept_path),
         _ptr(context_lens), _ptr(freed_slots), _ptr(kv_cache), slots, stride, _ptr(dest_slots), _ptr(dev_err),
         _stream_handle(stream)))
+
+
+def accept_commit(tree_parent: torch.Tensor, draft_tokens: torch.Tensor, target_tokens: torch.Tensor,
+                  page_table: torch.Tensor, seq_lens: torch.Tensor, accept_len: torch.Tensor,
+                  accept_path: torch.Tensor, context_lens: torch.Tensor, commit_tokens: torch.Tensor | None = None,
+                  freed_slots: torch.Tensor | None = None, kv_cache: torch.Tensor | None = None,
+                  dest_slots: torch.Tensor | None = None, dev_err: torch.Tensor | None = None, stream=None) -> None:
+    """Enqueue mla_accept_commit: tree_accept and commit_accepted in one launch."""
+    b, t = tree_parent.shape
+    for x, nm in ((tree_parent, "tree_parent"), (draft_tokens, "draft_tokens"), (target_tokens, "target_tokens"),
+                  (accept_path, "accept_path")):
+        _i32(x, (b, t), nm)
+    _need(page_table.dim() == 2 and page_table.shape[0] == b, "page_table must be [B, max_pages]")
+    max_pages = page_table.shape[1]
+    _i32(page_table, (b, max_pages), "page_table")
+    for x, nm in ((seq_lens, "seq_lens"), (accept_len, "accept_len"), (context_lens, "context_lens")):
+        _i32(x, (b,), nm)
+    for x, nm in ((commit_tokens, "commit_tokens"), (freed_slots, "freed_slots"), (dest_slots, "dest_slots")):
+        if x is not None:
+            _i32(x, (b, t), nm)
+    slots, stride = 0, 0
+    if kv_cache is not None:
+        _need(kv_cache.dtype == torch.bfloat16 and kv_cache.dim() == 2 and kv_cache.stride(1) == 1,
+              "kv_cache must be bf16 [slots, stride]")
+        slots, stride = kv_cache.shape[0], kv_cache.stride(0)
+    _check("mla_accept_commit", load_library().mla_accept_commit(
+        _ptr(tree_parent), _ptr(draft_tokens), _ptr(target_tokens), b, t, _ptr(page_table), max_pages,
+        _ptr(seq_lens), _ptr(accept_len), _ptr(accept_path), _ptr(commit_tokens), _ptr(context_lens),
+        _ptr(freed_slots), _ptr(kv_cache), slots, stride, _ptr(dest_slots), _ptr(dev_err), _stream_handle(stream)))
 
 
 def window_map(target_map: torch.Tensor, lens: torch.Tensor, window: int, page: int, draft_map: torch.Tensor,

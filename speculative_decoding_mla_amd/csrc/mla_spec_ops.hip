@@ -95,18 +95,18 @@ __device__ __forceinline__ void climb(int parent, bool f, int lane, int T, bool&
 
 // ---------------------------------------------------------------- greedy tree accept (one wave per request)
 
-__global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restrict__ parents,
-                                                         const int32_t* __restrict__ draft,
-                                                         const int32_t* __restrict__ target, int T,
-                                                         int32_t* __restrict__ accept_len,
-                                                         int32_t* __restrict__ path, int32_t* __restrict__ commit,
-                                                         uint32_t* err) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+struct Accepted {
+  uint64_t on_path;  // nodes of the kept path, root..kept node
+  int n_acc;         // committed tokens: depth of the kept node + 1
+};
+
+// The accept of request b by one wave (lane = node); writes accept_len, path
+// and (when set) commit as mla_tree_accept documents them.
+__device__ __forceinline__ Accepted accept_one(const AcceptLaunch& A, int T, int b, int lane) {
   const size_t base = static_cast<size_t>(b) * T;
-  const int p = checked_parent(parents + base, T, lane, err);
-  const int d = lane < T ? draft[base + lane] : 0;
-  const int tg = lane < T ? target[base + lane] : 0;
+  const int p = checked_parent(A.parents + base, T, lane, A.err);
+  const int d = lane < T ? A.draft[base + lane] : 0;
+  const int tg = lane < T ? A.target[base + lane] : 0;
   // a root is accepted; another node iff its draft equals the target's choice after its parent
   const int tg_parent = __shfl(tg, p >= 0 ? p : lane);
   const bool match = p < 0 || d == tg_parent;
@@ -124,92 +124,142 @@ __global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restri
   const uint32_t bhi = __shfl(static_cast<uint32_t>(anc >> 32), best);
   const uint64_t on_path = (static_cast<uint64_t>(bhi) << 32) | blo;
   const int n_acc = best_depth + 1;
-  if (lane == 0) accept_len[b] = n_acc;
+  if (lane == 0) A.accept_len[b] = n_acc;
   if (lane < T) {
     const bool mine = (on_path >> lane) & 1ull;
     const int pos = __popcll(on_path & ((1ull << lane) - 1ull));  // place on the path (root = 0)
-    if (mine) path[base + pos] = lane;
-    if (lane >= n_acc) path[base + lane] = -1;
-    if (commit != nullptr) {
-      if (mine && pos >= 1) commit[base + pos - 1] = d;
-      if (lane == best) commit[base + best_depth] = tg;
-      if (lane > best_depth) commit[base + lane] = -1;
+    if (mine) A.path[base + pos] = lane;
+    if (lane >= n_acc) A.path[base + lane] = -1;
+    if (A.commit != nullptr) {
+      if (mine && pos >= 1) A.commit[base + pos - 1] = d;
+      if (lane == best) A.commit[base + best_depth] = tg;
+      if (lane > best_depth) A.commit[base + lane] = -1;
     }
   }
+  return {on_path, n_acc};
+}
+
+__global__ __launch_bounds__(64) void tree_accept_kernel(AcceptLaunch A, int T) {
+  accept_one(A, T, blockIdx.x, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- commit of the accepted path (one workgroup per request)
 
 constexpr int kCommitThreads = 256;
 
-__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitLaunch C) {
-  __shared__ int32_t tree_slot[kMaxTreeNodes];
-  __shared__ int32_t path_s[kMaxTreeNodes];
-  __shared__ int32_t n_acc_s, c0_s;
-  __shared__ uint64_t on_path_s;
-  __shared__ __attribute__((aligned(16))) uint8_t rows_s[kMaxTreeNodes * kRowChunks * 16];
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+struct CommitLds {
+  int32_t tree_slot[kMaxTreeNodes];  // slots of the request's tree rows, node order
+  int32_t path[kMaxTreeNodes];       // accepted nodes, root first
+  uint64_t on_path;
+  int32_t n_acc, c0;
+  u32x4 rows[kMaxTreeNodes * kRowChunks];  // accepted rows in flight during a relocation
+};
+
+// One wave: the first committed position c0 = seq_len - T and the tree rows'
+// slots from the page table.
+__device__ __forceinline__ void load_tree_slots(const CommitLaunch& C, CommitLds& S, int b, int lane) {
+  const int T = C.nodes;
+  const int sl = C.seq_lens[b];
+  const int sl_c = min(max(sl, T), C.max_pages);
+  if (sl != sl_c && lane == 0) flag(C.err, MLA_DEVERR_INDEX_RANGE);
+  const int c0 = sl_c - T;
+  if (lane == 0) S.c0 = c0;
+  if (lane < T) S.tree_slot[lane] = C.page_table[static_cast<size_t>(b) * C.max_pages + c0 + lane];
+}
+
+// The whole workgroup, after S is filled and a barrier: relocation (every
+// accepted row is read into LDS before any is written), page-table entries,
+// released slots and the new context length.
+__device__ __forceinline__ void commit_rows(const CommitLaunch& C, CommitLds& S, int b, int tid) {
   const int T = C.nodes;
   const size_t tb = static_cast<size_t>(b) * T;
-  if (tid == 0) {
-    const int sl = C.seq_lens[b];
-    const int sl_c = min(max(sl, T), C.max_pages);
-    const int na = C.accept_len[b];
-    const int na_c = min(max(na, 1), T);
-    if (sl != sl_c || na != na_c) flag(C.err, MLA_DEVERR_INDEX_RANGE);
-    c0_s = sl_c - T;
-    n_acc_s = na_c;
-    on_path_s = 0ull;
-  }
-  __syncthreads();
-  const int c0 = c0_s, n_acc = n_acc_s;
+  const int c0 = S.c0, n_acc = S.n_acc;
   int32_t* row = C.page_table + static_cast<size_t>(b) * C.max_pages;
-  if (tid < T) {
-    tree_slot[tid] = row[c0 + tid];
-    if (tid < n_acc) {
-      int j = C.path[tb + tid];
-      if (j < 0 || j >= T) {
-        flag(C.err, MLA_DEVERR_INDEX_RANGE);
-        j = min(max(j, 0), T - 1);
-      }
-      path_s[tid] = j;
-      atomicOr(reinterpret_cast<unsigned long long*>(&on_path_s), 1ull << j);
-    }
-  }
-  __syncthreads();
-  // relocation: every accepted row is read into LDS before any is written
   if (C.dest != nullptr) {
     for (int t = tid; t < n_acc * kRowChunks; t += kCommitThreads) {
       const int k = t / kRowChunks, c = t - k * kRowChunks;
-      const int32_t src = tree_slot[path_s[k]];
+      const int32_t src = S.tree_slot[S.path[k]];
       u32x4 v = {0u, 0u, 0u, 0u};
       if (src >= 0 && src < C.num_slots) v = *reinterpret_cast<const u32x4*>(C.kv + src * C.row_bytes + c * 16);
-      *reinterpret_cast<u32x4*>(rows_s + t * 16) = v;
+      S.rows[t] = v;
     }
     __syncthreads();
     for (int t = tid; t < n_acc * kRowChunks; t += kCommitThreads) {
       const int k = t / kRowChunks, c = t - k * kRowChunks;
-      const int32_t src = tree_slot[path_s[k]];
+      const int32_t src = S.tree_slot[S.path[k]];
       const int32_t dst = C.dest[tb + k];
       const bool ok = src >= 0 && src < C.num_slots && dst >= 0 && dst < C.num_slots;
       if (!ok) {
         if (c == 0) flag(C.err, MLA_DEVERR_SLOT_RANGE);
         continue;
       }
-      *reinterpret_cast<u32x4*>(C.kv + dst * C.row_bytes + c * 16) = *reinterpret_cast<const u32x4*>(rows_s + t * 16);
+      *reinterpret_cast<u32x4*>(C.kv + dst * C.row_bytes + c * 16) = S.rows[t];
     }
   }
-  if (tid < n_acc) row[c0 + tid] = C.dest != nullptr ? C.dest[tb + tid] : tree_slot[path_s[tid]];
+  if (tid < n_acc) row[c0 + tid] = C.dest != nullptr ? C.dest[tb + tid] : S.tree_slot[S.path[tid]];
   if (tid < T && C.freed != nullptr) {
-    const uint64_t on_path = on_path_s;
+    const uint64_t on_path = S.on_path;
     const bool kept = (on_path >> tid) & 1ull;
     const uint64_t below = (tid == 0 ? 0ull : (~0ull >> (64 - tid)));
     const int pos = tid - __popcll(on_path & below);  // released nodes before this one
-    if (!kept) C.freed[tb + pos] = tree_slot[tid];
+    if (!kept) C.freed[tb + pos] = S.tree_slot[tid];
     if (tid >= T - n_acc) C.freed[tb + tid] = -1;
   }
   if (tid == 0) C.context_lens[b] = c0 + n_acc;
+}
+
+// Commit of a path written earlier (accept_len, path in global memory, range
+// checked): wave 0 reads the page table, wave 1 the path.
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitLaunch C) {
+  __shared__ CommitLds S;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int T = C.nodes;
+  if (wave == 0) {
+    load_tree_slots(C, S, b, lane);
+  } else if (wave == 1) {
+    const int na = C.accept_len[b];
+    const int n_acc = min(max(na, 1), T);
+    int j = lane < n_acc ? C.path[static_cast<size_t>(b) * T + lane] : 0;
+    const bool bad = na != n_acc || j < 0 || j >= T;
+    if (__any(bad) && lane == 0) flag(C.err, MLA_DEVERR_INDEX_RANGE);
+    j = min(max(j, 0), T - 1);
+    uint64_t bit = lane < n_acc ? 1ull << j : 0ull;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t lo = __shfl_xor(static_cast<uint32_t>(bit), o);
+      const uint32_t hi = __shfl_xor(static_cast<uint32_t>(bit >> 32), o);
+      bit |= (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+    if (lane < n_acc) S.path[lane] = j;
+    if (lane == 0) {
+      S.n_acc = n_acc;
+      S.on_path = bit;
+    }
+  }
+  __syncthreads();
+  commit_rows(C, S, b, tid);
+}
+
+// Accept and commit in one launch: wave 0 runs the accept while wave 1 reads
+// the page table; the commit takes the path from LDS.
+__global__ __launch_bounds__(kCommitThreads) void accept_commit_kernel(AcceptLaunch A, CommitLaunch C) {
+  __shared__ CommitLds S;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int T = C.nodes;
+  if (wave == 0) {
+    const Accepted a = accept_one(A, T, b, lane);
+    if (lane < T && ((a.on_path >> lane) & 1ull)) S.path[__popcll(a.on_path & ((1ull << lane) - 1ull))] = lane;
+    if (lane == 0) {
+      S.n_acc = a.n_acc;
+      S.on_path = a.on_path;
+    }
+  } else if (wave == 1) {
+    load_tree_slots(C, S, b, lane);
+  }
+  __syncthreads();
+  commit_rows(C, S, b, tid);
 }
 
 // ---------------------------------------------------------------- sliding-window map
@@ -431,16 +481,18 @@ hipError_t launch_kv_append(uint8_t* kv, int64_t num_slots, int64_t row_bytes, c
   return hipGetLastError();
 }
 
-hipError_t launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target, int batch, int T,
-                              int32_t* accept_len, int32_t* path, int32_t* commit, uint32_t* err,
-                              hipStream_t stream) {
-  hipLaunchKernelGGL(tree_accept_kernel, dim3(batch), dim3(64), 0, stream, parents, draft, target, T, accept_len,
-                     path, commit, err);
+hipError_t launch_tree_accept(const AcceptLaunch& A, int batch, int T, hipStream_t stream) {
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(batch), dim3(64), 0, stream, A, T);
   return hipGetLastError();
 }
 
 hipError_t launch_commit(const CommitLaunch& C, hipStream_t stream) {
   hipLaunchKernelGGL(commit_kernel, dim3(C.batch), dim3(kCommitThreads), 0, stream, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_commit(const AcceptLaunch& A, const CommitLaunch& C, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_commit_kernel, dim3(C.batch), dim3(kCommitThreads), 0, stream, A, C);
   return hipGetLastError();
 }
 

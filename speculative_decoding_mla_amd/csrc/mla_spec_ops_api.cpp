@@ -30,6 +30,38 @@ mla_status check_sparse(const mla_sparse_desc* d) {
   return MLA_OK;
 }
 
+// Checks shared by the two commit entry points; fills every field of C but
+// accept_len and path.
+mla_status commit_launch(int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                         int32_t num_nodes, int32_t* context_lens, int32_t* freed_slots, void* kv_cache,
+                         int64_t num_kv_slots, int64_t kv_row_stride, const int32_t* dest_slots, uint32_t* dev_err,
+                         mlav::CommitLaunch& C) {
+  if (page_table == nullptr || seq_lens == nullptr || context_lens == nullptr) return MLA_ERR_NULL;
+  if ((kv_cache == nullptr) != (dest_slots == nullptr)) return MLA_ERR_NULL;
+  if (batch < 1 || num_nodes < 1 || num_nodes > mlav::kMaxTreeNodes || max_pages < num_nodes) return MLA_ERR_SHAPE;
+  if (kv_cache != nullptr) {
+    if (num_kv_slots < 1 || num_kv_slots > std::numeric_limits<int32_t>::max() || kv_row_stride < mlav::kQkDim ||
+        (kv_row_stride % 8) != 0)
+      return MLA_ERR_SHAPE;
+    if (misaligned(kv_cache, 16)) return MLA_ERR_ALIGN;
+  }
+  C.page_table = page_table;
+  C.seq_lens = seq_lens;
+  C.accept_len = nullptr;
+  C.path = nullptr;
+  C.context_lens = context_lens;
+  C.freed = freed_slots;
+  C.kv = static_cast<uint8_t*>(kv_cache);
+  C.dest = dest_slots;
+  C.err = dev_err;
+  C.num_slots = num_kv_slots;
+  C.row_bytes = kv_row_stride * 2;
+  C.batch = batch;
+  C.nodes = num_nodes;
+  C.max_pages = max_pages;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,8 +139,8 @@ mla_status mla_tree_accept(const int32_t* tree_parent, const int32_t* draft_toke
       accept_path == nullptr)
     return MLA_ERR_NULL;
   if (batch < 1 || num_nodes < 1 || num_nodes > mlav::kMaxTreeNodes) return MLA_ERR_SHAPE;
-  return launched(mlav::launch_tree_accept(tree_parent, draft_tokens, target_tokens, batch, num_nodes, accept_len,
-                                           accept_path, commit_tokens, dev_err, stream));
+  const mlav::AcceptLaunch A{tree_parent, draft_tokens, target_tokens, accept_len, accept_path, commit_tokens, dev_err};
+  return launched(mlav::launch_tree_accept(A, batch, num_nodes, stream));
 }
 
 mla_status mla_commit_accepted(int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t batch,
@@ -116,33 +148,31 @@ mla_status mla_commit_accepted(int32_t* page_table, int32_t max_pages, const int
                                int32_t* context_lens, int32_t* freed_slots, void* kv_cache, int64_t num_kv_slots,
                                int64_t kv_row_stride, const int32_t* dest_slots, uint32_t* dev_err,
                                hipStream_t stream) {
-  if (page_table == nullptr || seq_lens == nullptr || accept_len == nullptr || accept_path == nullptr ||
-      context_lens == nullptr)
-    return MLA_ERR_NULL;
-  if ((kv_cache == nullptr) != (dest_slots == nullptr)) return MLA_ERR_NULL;
-  if (batch < 1 || num_nodes < 1 || num_nodes > mlav::kMaxTreeNodes || max_pages < num_nodes) return MLA_ERR_SHAPE;
-  if (kv_cache != nullptr) {
-    if (num_kv_slots < 1 || num_kv_slots > std::numeric_limits<int32_t>::max() || kv_row_stride < mlav::kQkDim ||
-        (kv_row_stride % 8) != 0)
-      return MLA_ERR_SHAPE;
-    if (misaligned(kv_cache, 16)) return MLA_ERR_ALIGN;
-  }
+  if (accept_len == nullptr || accept_path == nullptr) return MLA_ERR_NULL;
   mlav::CommitLaunch C;
-  C.page_table = page_table;
-  C.seq_lens = seq_lens;
+  const mla_status st = commit_launch(page_table, max_pages, seq_lens, batch, num_nodes, context_lens, freed_slots,
+                                      kv_cache, num_kv_slots, kv_row_stride, dest_slots, dev_err, C);
+  if (st != MLA_OK) return st;
   C.accept_len = accept_len;
   C.path = accept_path;
-  C.context_lens = context_lens;
-  C.freed = freed_slots;
-  C.kv = static_cast<uint8_t*>(kv_cache);
-  C.dest = dest_slots;
-  C.err = dev_err;
-  C.num_slots = num_kv_slots;
-  C.row_bytes = kv_row_stride * 2;
-  C.batch = batch;
-  C.nodes = num_nodes;
-  C.max_pages = max_pages;
   return launched(mlav::launch_commit(C, stream));
+}
+
+mla_status mla_accept_commit(const int32_t* tree_parent, const int32_t* draft_tokens, const int32_t* target_tokens,
+                             int32_t batch, int32_t num_nodes, int32_t* page_table, int32_t max_pages,
+                             const int32_t* seq_lens, int32_t* accept_len, int32_t* accept_path,
+                             int32_t* commit_tokens, int32_t* context_lens, int32_t* freed_slots, void* kv_cache,
+                             int64_t num_kv_slots, int64_t kv_row_stride, const int32_t* dest_slots,
+                             uint32_t* dev_err, hipStream_t stream) {
+  if (tree_parent == nullptr || draft_tokens == nullptr || target_tokens == nullptr || accept_len == nullptr ||
+      accept_path == nullptr)
+    return MLA_ERR_NULL;
+  mlav::CommitLaunch C;
+  const mla_status st = commit_launch(page_table, max_pages, seq_lens, batch, num_nodes, context_lens, freed_slots,
+                                      kv_cache, num_kv_slots, kv_row_stride, dest_slots, dev_err, C);
+  if (st != MLA_OK) return st;
+  const mlav::AcceptLaunch A{tree_parent, draft_tokens, target_tokens, accept_len, accept_path, commit_tokens, dev_err};
+  return launched(mlav::launch_accept_commit(A, C, stream));
 }
 
 mla_status mla_window_map(const int32_t* target_map, int32_t map_stride, const int32_t* lens, int32_t batch,

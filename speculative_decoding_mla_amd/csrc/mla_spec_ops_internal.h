@@ -9,6 +9,16 @@ namespace mlav {
 
 constexpr int kMaxTreeNodes = 64;  // draft trees are handled one node per lane of a wave
 
+struct AcceptLaunch {
+  const int32_t* parents;  // [B, T]
+  const int32_t* draft;    // [B, T]
+  const int32_t* target;   // [B, T]
+  int32_t* accept_len;     // [B] out
+  int32_t* path;           // [B, T] out
+  int32_t* commit;         // [B, T] out, nullable
+  uint32_t* err;           // nullable
+};
+
 struct CommitLaunch {
   int32_t* page_table;        // [B, max_pages], page size 1
   const int32_t* seq_lens;    // [B] verify lengths (tree rows included)
@@ -37,10 +47,9 @@ struct IndexerLaunch {
 
 hipError_t launch_kv_append(uint8_t* kv, int64_t num_slots, int64_t row_bytes, const uint8_t* rows,
                             const int32_t* loc, int n, uint32_t* err, hipStream_t stream);
-hipError_t launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target, int batch, int T,
-                              int32_t* accept_len, int32_t* path, int32_t* commit, uint32_t* err,
-                              hipStream_t stream);
+hipError_t launch_tree_accept(const AcceptLaunch& A, int batch, int T, hipStream_t stream);
 hipError_t launch_commit(const CommitLaunch& C, hipStream_t stream);
+hipError_t launch_accept_commit(const AcceptLaunch& A, const CommitLaunch& C, hipStream_t stream);
 hipError_t launch_window_map(const int32_t* target_map, int map_stride, const int32_t* lens, int batch, int W,
                              int P, int32_t* draft_map, int32_t* compact_lens, uint32_t* err, hipStream_t stream);
 hipError_t launch_indexer(const IndexerLaunch& I, hipStream_t stream);

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol():
                           "mla_verify_abi_version"}
     ops = declared_functions(HEADER_OPS)
     assert set(ops) == {"mla_sparse_decode_workspace_bytes", "mla_sparse_decode", "mla_kv_append",
-                        "mla_tree_accept", "mla_commit_accepted", "mla_window_map", "mla_indexer_logits"}
+                        "mla_tree_accept", "mla_commit_accepted", "mla_accept_commit", "mla_window_map",
+                        "mla_indexer_logits"}
     lib = ctypes.CDLL(bd.LIB_PATH)
     for n in names + ops:
         assert hasattr(lib, n), n
@@ -190,6 +191,13 @@ def test_step_entry_points_check_arguments():
     assert lib.mla_commit_accepted(a, 100, a, 1, 4, a, a, a, None, a, 10, 576, None, None, None) == -1
     assert lib.mla_commit_accepted(a, 3, a, 1, 4, a, a, a, None, None, 0, 0, None, None, None) == -2
     assert lib.mla_commit_accepted(a, 100, a, 1, 4, a, a, a, None, a + 8, 10, 576, a, None, None) == -5
+    # accept + commit in one launch: the checks of both
+    assert lib.mla_accept_commit(None, a, a, 1, 4, a, 100, a, a, a, None, a, None, None, 0, 0, None, None, None) == -1
+    assert lib.mla_accept_commit(a, a, a, 1, 4, a, 100, a, None, a, None, a, None, None, 0, 0, None, None, None) == -1
+    assert lib.mla_accept_commit(a, a, a, 1, 4, a, 100, a, a, a, None, a, None, a, 10, 576, None, None, None) == -1
+    assert lib.mla_accept_commit(a, a, a, 1, 65, a, 100, a, a, a, None, a, None, None, 0, 0, None, None, None) == -2
+    assert lib.mla_accept_commit(a, a, a, 1, 4, a, 3, a, a, a, None, a, None, None, 0, 0, None, None, None) == -2
+    assert lib.mla_accept_commit(a, a, a, 1, 4, a, 100, a, a, a, None, a, None, a + 8, 10, 576, a, None, None) == -5
     # window map
     assert lib.mla_window_map(a, 100, a, 1, 0, 64, a, None, None, None) == -2
     assert lib.mla_window_map(None, 100, a, 1, 4096, 64, a, None, None, None) == -1

@@ -249,6 +249,82 @@ def test_commit_clamps_and_flags():
     assert ctx[0] == c.seq_lens[0] - 8 + 8 and ctx[1] == c.seq_lens[1] - 8 + n[1]
 
 
+# ================================================================== accept and commit in one launch
+
+def run_accept_commit(c, dest=None, kv=None, with_commit=True, seq_lens=None, parents=None):
+    b, t = c.tree_parent.shape
+    pt = _t(c.page_table)
+    n = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    path = torch.full((b, t), -7, dtype=torch.int32, device="cuda")
+    com = torch.full((b, t), -7, dtype=torch.int32, device="cuda") if with_commit else None
+    ctx = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    freed = torch.full((b, t), -7, dtype=torch.int32, device="cuda")
+    kv_t = None if kv is None else bf16(kv).cuda()
+    err = _err()
+    mv.accept_commit(_t(c.tree_parent if parents is None else parents), _t(c.draft_tokens), _t(c.target_tokens), pt,
+                     _t(c.seq_lens if seq_lens is None else seq_lens), n, path, ctx, com, freed, kv_t,
+                     None if dest is None else _t(dest), err)
+    torch.cuda.synchronize()
+    kv_out = None if kv is None else kv_t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return (n.cpu().numpy(), path.cpu().numpy(), None if com is None else com.cpu().numpy(), pt.cpu().numpy(),
+            ctx.cpu().numpy(), freed.cpu().numpy(), kv_out, int(err.item()))
+
+
+@pytest.mark.parametrize("tree", ["uniform", "chain", "depth8", "forest"])
+def test_accept_commit_matches_oracle(tree):
+    """One launch equals the oracle's accept followed by its commit."""
+    for seed, t, match in [(1, 1, 0.5), (2, 9, 0.9), (3, 16, 0.0), (4, 32, 0.85), (5, 63, 0.7), (6, 64, 1.0)]:
+        c = accept_case(seed * 17, batch=6, nodes=t, tree=tree, match=match, pool=100_000)
+        say(f"accept_commit tree={tree} seed={seed} T={t}")
+        n, path, com, pt, ctx, freed, _, err = run_accept_commit(c)
+        rn, rp, rc = so.tree_accept(c.tree_parent, c.draft_tokens, c.target_tokens)
+        rpt, rctx, rfreed, _ = so.commit_accepted(c.page_table, c.seq_lens, t, rn, rp)
+        assert err == 0
+        assert np.array_equal(n, rn) and np.array_equal(path, rp) and np.array_equal(com, rc), (tree, seed, t)
+        assert np.array_equal(pt, rpt) and np.array_equal(ctx, rctx) and np.array_equal(freed, rfreed), (tree, seed, t)
+
+
+def test_accept_commit_relocation_matches_oracle():
+    rng = np.random.default_rng(9)
+    for seed, t, overlap in [(1, 9, False), (2, 64, True), (3, 32, False), (4, 16, True)]:
+        c = accept_case(seed * 29, batch=4, nodes=t, match=0.9, pool=30_000, contexts=[500, 9, 1200, 77])
+        kv = rng.integers(0, 65535, size=(30_000, 576), dtype=np.uint16)
+        if overlap:
+            dest = np.stack([np.sort(c.page_table[b, c.seq_lens[b] - t:c.seq_lens[b]]) for b in range(4)]).astype(np.int32)
+        else:
+            used = set(c.page_table[c.page_table >= 0].tolist())
+            free = np.array(sorted(set(range(30_000)) - used), np.int32)
+            dest = free[:4 * t].reshape(4, t)
+        say(f"accept_commit relocation seed={seed} T={t} overlap={overlap}")
+        n, path, com, pt, ctx, freed, kv_out, err = run_accept_commit(c, dest, kv, with_commit=False)
+        rn, rp, _ = so.tree_accept(c.tree_parent, c.draft_tokens, c.target_tokens)
+        rpt, rctx, rfreed, rkv = so.commit_accepted(c.page_table, c.seq_lens, t, rn, rp, dest_slots=dest, kv_bits=kv)
+        assert err == 0
+        assert np.array_equal(n, rn) and np.array_equal(path, rp)
+        assert np.array_equal(pt, rpt) and np.array_equal(ctx, rctx) and np.array_equal(freed, rfreed)
+        assert np.array_equal(kv_out, rkv), (seed, t, overlap)
+
+
+def test_accept_commit_flags():
+    c = accept_case(92, batch=2, nodes=10, match=1.0, pool=20_000, contexts=[40, 50])
+    # a parent that is not an earlier node is read as a root
+    par = c.tree_parent.copy()
+    par[1, 6] = 8
+    n, path, com, pt, ctx, freed, _, err = run_accept_commit(c, parents=par)
+    assert err & mv.DEVERR_BAD_PARENT
+    par[1, 6] = -1
+    rn, rp, rc = so.tree_accept(par, c.draft_tokens, c.target_tokens)
+    rpt, rctx, rfreed, _ = so.commit_accepted(c.page_table, c.seq_lens, 10, rn, rp)
+    assert np.array_equal(n, rn) and np.array_equal(path, rp) and np.array_equal(com, rc)
+    assert np.array_equal(pt, rpt) and np.array_equal(ctx, rctx) and np.array_equal(freed, rfreed)
+    # a length below T is clamped to T (first committed position 0)
+    sl = c.seq_lens.copy()
+    sl[0] = 3
+    n, path, com, pt, ctx, freed, _, err = run_accept_commit(c, seq_lens=sl)
+    assert err & mv.DEVERR_INDEX_RANGE
+    assert ctx[0] == n[0] and ctx[1] == c.seq_lens[1] - 10 + n[1]
+
+
 # ================================================================== sliding-window map
 
 def test_window_map_bit_exact():
@@ -342,10 +418,12 @@ def test_indexer_bad_block_flagged():
 
 # ================================================================== capture of the step around verify
 
-def test_append_accept_commit_graph_replays():
-    """KV append -> tree accept -> commit captured in one hipGraph; every
-    replay (fresh inputs copied in by kernels inside the graph, eager work and
-    synchronisations between replays) matches the oracle bit for bit."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_append_accept_commit_graph_replays(fused):
+    """KV append -> tree accept -> commit (two launches, or one with fused)
+    captured in one hipGraph; every replay (fresh inputs copied in by kernels
+    inside the graph, eager work and synchronisations between replays) matches
+    the oracle bit for bit."""
     t, b = 16, 4
     c = accept_case(808, batch=b, nodes=t, match=0.85, pool=40_000, contexts=[300, 4000, 17, 999])
     rng = np.random.default_rng(8)
@@ -367,8 +445,11 @@ def test_append_accept_commit_graph_replays():
         kv.copy_(kv0_t)
         pt.copy_(pt0)
         mv.kv_append(kv, rows_t, loc_t)
-        mv.tree_accept(par, drf, tgt, n, path)
-        mv.commit_accepted(pt, sl, t, n, path, ctx, freed)
+        if fused:
+            mv.accept_commit(par, drf, tgt, pt, sl, n, path, ctx, None, freed)
+        else:
+            mv.tree_accept(par, drf, tgt, n, path)
+            mv.commit_accepted(pt, sl, t, n, path, ctx, freed)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
