@@ -46,7 +46,7 @@ typedef struct {
   int32_t topk;          /* K >= 1: width of a row of `indices` */
   int32_t nsplit;        /* >= 1: splits of each index list (results do not depend on it beyond rounding) */
   int64_t num_kv_slots;  /* rows in kv_cache */
-  int64_t kv_row_stride; /* elements between kv_cache rows: >= 576, multiple of 8 */
+  int64_t kv_row_stride; /* elements between kv_cache rows: >= 576, multiple of 8, <= 2^30 */
   float sm_scale;
 } mla_sparse_desc;
 

@@ -91,7 +91,7 @@ typedef struct {
                             (one at least each; equal lengths give nsplit each). Results do not
                             depend on it beyond rounding. */
   int64_t num_kv_slots;  /* rows in kv_cache; slots >= this are out of range */
-  int64_t kv_row_stride; /* elements between consecutive kv_cache rows: >= 576, multiple of 8 */
+  int64_t kv_row_stride; /* elements between consecutive kv_cache rows: >= 576, multiple of 8, <= 2^30 */
   float sm_scale;        /* softmax scale applied to q.k (1/sqrt(192) for 128 nope + 64 rope) */
 } mla_verify_desc;
 

@@ -22,6 +22,7 @@ mla_status check_sparse(const mla_sparse_desc* d) {
   if (d->head_dim_qk != mlav::kQkDim || d->head_dim_v != mlav::kVDim) return MLA_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->num_heads < 1 || d->topk < 1 || d->nsplit < 1 || d->num_kv_slots < 1) return MLA_ERR_SHAPE;
   if (d->kv_row_stride < mlav::kQkDim || (d->kv_row_stride % 8) != 0) return MLA_ERR_SHAPE;
+  if (d->kv_row_stride > mlav::kMaxRowStride) return MLA_ERR_SHAPE;
   if (!std::isfinite(d->sm_scale)) return MLA_ERR_SHAPE;
   if (d->num_kv_slots > std::numeric_limits<int32_t>::max() || d->num_heads > (1 << 20)) return MLA_ERR_SHAPE;
   const mlav::RowPlan rp = mlav::plan_rows(1, d->num_heads);

@@ -29,6 +29,7 @@ mla_status check_desc(const mla_verify_desc* d) {
       d->max_pages < 1 || d->nsplit < 1 || d->num_kv_slots < 1)
     return MLA_ERR_SHAPE;
   if (d->kv_row_stride < mlav::kQkDim || (d->kv_row_stride % 8) != 0) return MLA_ERR_SHAPE;
+  if (d->kv_row_stride > mlav::kMaxRowStride) return MLA_ERR_SHAPE;
   if (!std::isfinite(d->sm_scale)) return MLA_ERR_SHAPE;
   // Keys, slots and launch sizes are indexed with 32-bit integers on the device.
   const int64_t capacity = static_cast<int64_t>(d->max_pages) * d->page_size;

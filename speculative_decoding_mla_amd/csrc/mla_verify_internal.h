@@ -11,6 +11,7 @@ constexpr int kVDim = 512;        // V = leading 512 entries of the latent row
 constexpr int kMaxNodes = 64;     // ancestor sets are 64-bit masks
 constexpr int kCusPerDevice = 256;  // MI355X
 constexpr int kMaxColParts = 4;     // partial-lse records per (split, row): one per column part
+constexpr int64_t kMaxRowStride = int64_t{1} << 30;  // bf16 entries: row bytes stay below 2^31
 constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block of (node, head) rows per wave
 constexpr int kHeaderBytes = 256; // workspace header; word 0 is the device error word
 

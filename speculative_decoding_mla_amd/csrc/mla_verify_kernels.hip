@@ -115,6 +115,20 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// A key row's 1 KiB latent part: 16 bytes per lane from the wave-uniform row
+// address plus the lane offset lane16 ^ x into LDS at lds_base + lds_off +
+// 16*lane. The xor sits between the M0 write and the load, which needs one
+// wait state after it.
+__device__ __forceinline__ void dma16_row(const void* row, uint32_t lane16, uint32_t x, uint32_t lds_base,
+                                          uint32_t lds_off) {
+  uint32_t voff;
+  asm volatile("s_add_u32 m0, %2, %3\n\tv_xor_b32 %0, %4, %5\n\tglobal_load_lds_dwordx4 %0, %1"
+               : "=&v"(voff)
+               : "s"(row), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(__builtin_amdgcn_readfirstlane(lds_off)),
+                 "s"(__builtin_amdgcn_readfirstlane(x)), "v"(lane16)
+               : "memory", "m0", "scc");
+}
+
 // Same, from a wave-uniform base address plus a per-lane 32-bit offset.
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -132,15 +146,6 @@ __device__ __forceinline__ void store_agent8(T* p, const T& v) {
   static_assert(sizeof(T) == 8, "8-byte values");
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// v ^ s computed where it is used: as volatile asm it is never hoisted out of
-// a loop, so loop-invariant lane offsets are rebuilt (one VALU operation)
-// instead of held in registers across the tile loop.
-__device__ __forceinline__ uint32_t xor_here(uint32_t v, uint32_t s) {
-  uint32_t r;
-  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(v));
-  return r;
 }
 
 // f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{}): a
@@ -357,6 +362,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 
   const uint32_t lds_kv = lds_addr(kv_s);
   const uint32_t lane16 = lane * 16;
+  const uint32_t row_bytes32 = static_cast<uint32_t>(L.kv_row_bytes);  // < 2^31 (checked on the host)
 
   const int n = min(max(n_raw, kSparse ? 0 : T), L.capacity);
   if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
@@ -686,8 +692,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
         const uint32_t stage = lds_kv + (t % kStages) * kTileBytes;
         const bool all_latent = NW == 3 ? i < 10 : i < kKeysPerTile / NW;
         if (all_latent) {  // row address in SGPRs, lane offset in a VGPR
-          const uint8_t* row = L.kv + static_cast<size_t>(__builtin_amdgcn_readfirstlane(slot)) * L.kv_row_bytes;
-          dma16_sbase(row, xor_here(lane16, swz(ins) << 4), stage + ins * kLatentBytes);
+          const uint32_t s32 = __builtin_amdgcn_readfirstlane(slot);  // >= 0
+          dma16_row(L.kv + static_cast<uint64_t>(s32) * row_bytes32, lane16, swz(ins) << 4, stage,
+                    ins * kLatentBytes);
         } else {  // rope parts, or (NW = 3, load 10) either kind: selects, not branches
           const bool latent = ins < kKeysPerTile;
           const int g = ins - kKeysPerTile;
@@ -695,7 +702,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
           const uint32_t chunk =
               latent ? (lane16 ^ (swz(ins) << 4)) : ((kVDim / 8 + ((lane & 7) ^ swz(rkey))) << 4);
           const uint32_t dst = stage + (latent ? ins * kLatentBytes : kRopeBase + g * 1024);
-          dma16(L.kv + static_cast<size_t>(static_cast<uint32_t>(slot)) * L.kv_row_bytes + chunk, dst);
+          dma16(L.kv + static_cast<uint64_t>(static_cast<uint32_t>(slot)) * row_bytes32 + chunk, dst);
         }
       };
       auto issue_tile = [&](int t) {

@@ -73,7 +73,8 @@ def test_workspace_formula():
     (dict(num_nodes=0), -2), (dict(num_nodes=65), -2), (dict(batch=0), -2), (dict(num_heads=0), -2),
     (dict(nsplit=0), -2), (dict(max_pages=0), -2), (dict(num_kv_slots=0), -2),
     (dict(page_size=3), -3), (dict(page_size=0), -3), (dict(head_dim_qk=512), -3), (dict(head_dim_v=576), -3),
-    (dict(kv_row_stride=570), -2), (dict(kv_row_stride=580), -2), (dict(max_pages=3, num_nodes=4), -2),
+    (dict(kv_row_stride=570), -2), (dict(kv_row_stride=580), -2), (dict(kv_row_stride=(1 << 30) + 8), -2),
+    (dict(max_pages=3, num_nodes=4), -2),
 ])
 def test_bad_descriptor_rejected(kw, status):
     d = _desc(**kw)
@@ -151,7 +152,8 @@ def test_sparse_workspace_matches_verify_with_one_node():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), -2), (dict(num_heads=0), -2), (dict(topk=0), -2), (dict(nsplit=0), -2),
-    (dict(num_kv_slots=0), -2), (dict(kv_row_stride=570), -2), (dict(head_dim_qk=512), -3), (dict(head_dim_v=576), -3),
+    (dict(num_kv_slots=0), -2), (dict(kv_row_stride=570), -2), (dict(kv_row_stride=(1 << 30) + 8), -2),
+    (dict(head_dim_qk=512), -3), (dict(head_dim_v=576), -3),
 ])
 def test_sparse_bad_descriptor_rejected(kw, status):
     lib = bd.load_library()
