@@ -29,14 +29,16 @@
 //  * O^T += V^T P^T on the same MFMA; the V^T operand is read straight from the
 //    row-major tile with ds_read_b64_tr_b16 (no transposed copy).
 //  * Softmax in log2 units against a fixed per-row reference, set from the
-//    first tile with a visible key (its max + kRefLift). Weights exp2(s - ref)
+//    split's first tile (its max + kRefLift) and folded into the scaling of
+//    the scores, so a weight is one exp2. Weights exp2(s - ref)
 //    are accumulated without ever rescaling the accumulator, which therefore
 //    only sees MFMA writes and stays in AGPRs. fp32 and bf16 share an 8-bit
 //    exponent, so scores from ~94 below to kRefHead above the reference are
 //    exact in relative terms; anything lower is negligible next to the row
 //    max. Should a score rise beyond the reference + kRefHead (a gap of over
 //    128 in log2 units, ~89 in natural units: not seen with attention scores
-//    of ordinary range), the workgroup recomputes its split: one pass for the
+//    of ordinary range), or should a row that the first tile showed no key
+//    see one later, the workgroup recomputes its split: one pass for the
 //    exact row max, one accumulating against it. P is rounded to bf16 for the
 //    MFMA; the output normaliser sums those rounded weights (a convex
 //    combination) while the lse sums the fp32 weights.
@@ -85,6 +87,7 @@ constexpr int kQSteps = kQkDim / 16;                               // 36 k-steps
 constexpr int kColBlocks = kVDim / 32;                             // 16
 constexpr float kRefLift = 32.0f;  // log2 units: reference above the first visible tile max
 constexpr float kRefHead = 96.0f;  // log2 units: largest weight kept is 2^kRefHead
+constexpr float kHeadWeight = 0x1p96f;  // 2^kRefHead
 
 // 16-byte chunk permutation inside a 128-byte group, keyed by the key's index
 // in the tile: 8 consecutive keys hit 8 distinct slots (K reads), and the
@@ -301,7 +304,7 @@ template <int V>
 struct PassMode {
   static constexpr int value = V;
 };
-constexpr int kPassAdaptive = 0;  // accumulate; reference = first visible tile max + kRefLift
+constexpr int kPassAdaptive = 0;  // accumulate; reference = the split's first tile max + kRefLift
 constexpr int kPassMaxOnly = 1;   // scores only: exact row max over the split
 constexpr int kPassFixed = 2;     // accumulate against a given reference
 
@@ -445,6 +448,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   float l_sum = 0.f;        // sum of fp32 weights (this lane's half of the keys)
   float l_pb = 0.f;         // sum of bf16-rounded weights
   bool overflow = false;    // a score left the range the reference can absorb
+  float mu = 0.f;           // shift folded into the scaled scores: the reference once set, else 0
+  bool unset = false;       // no reference after the split's first tile (set only in the adaptive pass)
 
   // ---- building blocks of the tile pipeline
   // K fragment of k-step ks (dims 16ks..16ks+15 of key lane%32).
@@ -502,77 +507,73 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     const uint32_t vsh = vis >> (4 * hsel);
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      tsc[j] = ((vsh >> (8 * (j >> 2) + (j & 3))) & 1u) ? acc[j] * L.scale_log2 : -INFINITY;
+      tsc[j] = ((vsh >> (8 * (j >> 2) + (j & 3))) & 1u) ? fmaf(acc[j], L.scale_log2, -mu) : -INFINITY;
+    return (vsh & 0x0f0f0f0fu) != 0u;  // this lane sees a key of the tile
   };
 
-  // Softmax of one tile against the row's reference, cut into 19 pieces so
-  // that it can be spread between the MFMAs of the next tile's scores.
-  // Pieces 0-8: row max; 9: reference; 10-17: weights of two elements each;
-  // 18: sums and the P^T B operands of the two 16-key halves.
+  // Softmax of one tile, cut into pieces so that it can be spread between the
+  // MFMAs of the next tile's scores. The scores arrive already shifted by the
+  // row's reference (mu), so a weight is a single exp2.
+  // Exact-max pass (kPassMaxOnly): pieces 0-8 row max, 9 running max.
+  // Accumulating passes: pieces 0-7 weights of two elements each, 8 sums, the
+  // P^T B operands of the two 16-key halves and the overflow check.
   struct SoftmaxState {
-    float mx, mu, ts, tb;
+    float mx, ts, tb;
     bf16x2 pb2[8];
   };
+  auto softmax_pieces = [](auto mode_tag) { return decltype(mode_tag)::value == kPassMaxOnly ? 10 : 9; };
   auto softmax_piece = [&](auto mode_tag, int piece, SoftmaxState& sm, const float (&tsc)[16], bf16x8 (&pf)[2]) {
     constexpr int kMode = decltype(mode_tag)::value;
-    if (piece == 0) {
-      sm.mx = fmaxf(tsc[0], tsc[1]);
-    } else if (piece < 8) {
-      sm.mx = fmaxf(sm.mx, fmaxf(tsc[2 * piece], tsc[2 * piece + 1]));
-    } else if (piece == 8) {
-      sm.mx = fmaxf(sm.mx, xor32(sm.mx));
-    } else if (piece == 9) {
-      if constexpr (kMode == kPassMaxOnly) {
+    if constexpr (kMode == kPassMaxOnly) {
+      if (piece == 0) {
+        sm.mx = fmaxf(tsc[0], tsc[1]);
+      } else if (piece < 8) {
+        sm.mx = fmaxf(sm.mx, fmaxf(tsc[2 * piece], tsc[2 * piece + 1]));
+      } else if (piece == 8) {
+        sm.mx = fmaxf(sm.mx, xor32(sm.mx));
+      } else if (piece == 9) {
         m_max = fmaxf(m_max, sm.mx);
-      } else {
-        if constexpr (kMode == kPassAdaptive) {
-          // The first visible tile fixes the reference. Lifting it by
-          // kRefLift leaves room for scores up to kRefLift + kRefHead above
-          // that tile's max before a weight could overflow.
-          // (-inf + kRefLift stays -inf: a fully masked tile leaves it unset)
-          m_ref = m_ref == -INFINITY ? sm.mx + kRefLift : m_ref;
-          overflow |= sm.mx > m_ref + kRefHead;
-        }
-        sm.mu = m_ref == -INFINITY ? 0.f : m_ref;
-        sm.ts = 0.f;
-        sm.tb = 0.f;
       }
-    } else if (kMode != kPassMaxOnly && piece < 18) {
-      const int k = piece - 10;
-      const float p0 = __builtin_amdgcn_exp2f(tsc[2 * k] - sm.mu);
-      const float p1 = __builtin_amdgcn_exp2f(tsc[2 * k + 1] - sm.mu);
-      sm.ts += p0 + p1;
-      sm.pb2[k] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-      // the rounded pair summed in one bf16 dot product with (1, 1)
-      sm.tb = __builtin_amdgcn_fdot2_f32_bf16(sm.pb2[k], bf16x2{static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)},
-                                              sm.tb, false);
-    } else if (kMode != kPassMaxOnly && piece == 18) {
-      l_sum += sm.ts;
-      l_pb += sm.tb;
+    } else {
+      if (piece < 8) {
+        const float p0 = __builtin_amdgcn_exp2f(tsc[2 * piece]);
+        const float p1 = __builtin_amdgcn_exp2f(tsc[2 * piece + 1]);
+        sm.ts = piece == 0 ? p0 + p1 : sm.ts + (p0 + p1);
+        sm.pb2[piece] = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+        // the rounded pair summed in one bf16 dot product with (1, 1)
+        sm.tb = __builtin_amdgcn_fdot2_f32_bf16(sm.pb2[piece],
+                                                bf16x2{static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)},
+                                                piece == 0 ? 0.f : sm.tb, false);
+      } else if (piece == 8) {
+        l_sum += sm.ts;
+        l_pb += sm.tb;
+        // A weight beyond 2^kRefHead (the lane's tile sum is a bound from
+        // above) means a score the reference cannot absorb.
+        if constexpr (kMode == kPassAdaptive) overflow |= !(sm.ts <= kHeadWeight);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        pf[kk] = bf16x8{sm.pb2[4 * kk][0], sm.pb2[4 * kk][1], sm.pb2[4 * kk + 1][0], sm.pb2[4 * kk + 1][1],
-                        sm.pb2[4 * kk + 2][0], sm.pb2[4 * kk + 2][1], sm.pb2[4 * kk + 3][0], sm.pb2[4 * kk + 3][1]};
+        for (int kk = 0; kk < 2; ++kk)
+          pf[kk] = bf16x8{sm.pb2[4 * kk][0], sm.pb2[4 * kk][1], sm.pb2[4 * kk + 1][0], sm.pb2[4 * kk + 1][1],
+                          sm.pb2[4 * kk + 2][0], sm.pb2[4 * kk + 2][1], sm.pb2[4 * kk + 3][0], sm.pb2[4 * kk + 3][1]};
+      }
     }
   };
   // Pins the values a piece produced at this point of the instruction stream
   // (the compiler may not sink the piece past the MFMA that follows).
   auto anchor = [&](auto mode_tag, int piece, SoftmaxState& sm, bf16x8 (&pf)[2]) {
     constexpr int kMode = decltype(mode_tag)::value;
-    if (piece <= 8) {
+    if constexpr (kMode == kPassMaxOnly) {
       asm volatile("" : "+v"(sm.mx));
-    } else if (piece == 9) {
-      if constexpr (kMode != kPassMaxOnly) asm volatile("" : "+v"(sm.mu), "+v"(sm.ts), "+v"(sm.tb));
-    } else if (kMode != kPassMaxOnly && piece < 18) {
-      asm volatile("" : "+v"(sm.ts), "+v"(sm.tb), "+v"(sm.pb2[piece - 10]));
-    } else if (kMode != kPassMaxOnly && piece == 18) {
+    } else if (piece < 8) {
+      asm volatile("" : "+v"(sm.ts), "+v"(sm.tb), "+v"(sm.pb2[piece]));
+    } else if (piece == 8) {
       asm volatile("" : "+v"(pf[0]), "+v"(pf[1]));
     }
   };
   auto softmax = [&](auto mode_tag, const float (&tsc)[16], bf16x8 (&pf)[2]) {
     SoftmaxState sm;
 #pragma unroll
-    for (int piece = 0; piece < 19; ++piece) softmax_piece(mode_tag, piece, sm, tsc, pf);
+    for (int piece = 0; piece < 10; ++piece)
+      if (piece < softmax_pieces(mode_tag)) softmax_piece(mode_tag, piece, sm, tsc, pf);
   };
 
   // V^T fragment of PV step i (column block cp*kCB + i%kCB, keys
@@ -618,6 +619,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       l_sum = 0.f;
       l_pb = 0.f;
     }
+    mu = kMode == kPassFixed && m_ref != -INFINITY ? m_ref : 0.f;
     for (int w0 = k0; w0 < k1; w0 += kSlotCap) {
       const int wn = min(k1 - w0, kSlotCap);
       const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
@@ -720,7 +722,26 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       else wait_vmcnt<0>();
       lds_barrier();
       float tsc[16];
-      scale_mask(qk(kv_s), visible_bits(w0, wn, 0), tsc);
+      const bool sees = scale_mask(qk(kv_s), visible_bits(w0, wn, 0), tsc);
+      if constexpr (kMode == kPassAdaptive) {
+        if (w0 == k0) {
+          // The split's first tile fixes each row's reference: its max +
+          // kRefLift (room for scores up to kRefLift + kRefHead above it).
+          // A row it shows no key to keeps none; should a later tile show
+          // it one, the split takes the exact path.
+          float mx = tsc[0];
+#pragma unroll
+          for (int j = 1; j < 16; ++j) mx = fmaxf(mx, tsc[j]);
+          mx = fmaxf(mx, xor32(mx));
+          m_ref = mx + kRefLift;  // -inf stays -inf
+          mu = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) tsc[j] -= mu;  // these scores were taken unshifted
+          unset = m_ref == -INFINITY;
+        } else {
+          overflow |= unset && sees;
+        }
+      }
 
       // Step t: scores of tile t+1, softmax and PV of tile t, loads of tile
       // t+3. The steps that issue loads and the last two (which issue none)
@@ -757,9 +778,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
             constexpr int ks = decltype(ks_c)::value;
             qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
             if constexpr (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st1, ks + 4);
-            if constexpr (ks < 19) {
-              softmax_piece(mode_tag, ks, sm, tsc, pf);
-              anchor(mode_tag, ks, sm, pf);
+            if constexpr (ks % 2 == 0 && ks / 2 < (kMode == kPassMaxOnly ? 10 : 9)) {
+              softmax_piece(mode_tag, ks / 2, sm, tsc, pf);
+              anchor(mode_tag, ks / 2, sm, pf);
             }
             if constexpr (dma_next) {
               constexpr int ahead = ks + kSlotLead;  // step whose load needs its slot now
@@ -784,7 +805,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
             for (int k = 0; k < kMaskPer; ++k) {
               const int m = i * kMaskPer + k;
               if (m < 16) {
-                tsc[m] = acc[m] * L.scale_log2;
+                tsc[m] = fmaf(acc[m], L.scale_log2, -mu);
                 asm volatile("" : "+v"(tsc[m]));
               }
             }
@@ -804,6 +825,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
               tsc[m] = ((vsh >> (8 * (m >> 2) + (m & 3))) & 1u) ? tsc[m] : -INFINITY;
               asm volatile("" : "+v"(tsc[m]));  // (keeps the branch: no speculative selects)
             }
+            if constexpr (kMode == kPassAdaptive) overflow |= unset && (vsh & 0x0f0f0f0fu) != 0u;
+          } else {
+            if constexpr (kMode == kPassAdaptive) overflow |= unset;
           }
         }
       };
@@ -821,7 +845,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 
   run_pass(PassMode<kPassAdaptive>{});
   // Workgroup-wide vote: did any row see a score the reference cannot absorb?
-  if (lane == 0) over_s[wid] = __any(overflow);
+  // (the vote is taken by the whole wave: inside `lane == 0` it would see only
+  // that lane's row)
+  const bool wave_over = __any(overflow);
+  if (lane == 0) over_s[wid] = wave_over;
   lds_barrier();
   bool any_over = false;
 #pragma unroll

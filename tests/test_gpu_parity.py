@@ -211,12 +211,16 @@ def test_hot_context_key_exact(hot_pos, gap_rope):
     assert np.all(o[..., 2:] == 0)
 
 
-@pytest.mark.parametrize("page_size", [1, 4])
-def test_hot_tree_key_follows_ancestors(page_size):
+@pytest.mark.parametrize("page_size,gap_rope", [(1, 16.0), (4, 16.0), (1, 32.0)])
+def test_hot_tree_key_follows_ancestors(page_size, gap_rope):
+    """A hot tree key reaches exactly the nodes it is an ancestor of. With gap
+    32 only those rows take the recompute path's trigger (their score is more
+    than 128 above the reference in log2 units) while the others, row 0
+    among them for j > 0, do not: the workgroup's vote must hear every row."""
     ctx, nodes = 300, 8
     for j in range(nodes):
-        case, hot_slot = _probe(ctx + j, ctx=ctx, nodes=nodes, page_size=page_size)
-        say(f"hot tree key j={j} ps={page_size}")
+        case, hot_slot = _probe(ctx + j, ctx=ctx, nodes=nodes, page_size=page_size, gap_rope=gap_rope)
+        say(f"hot tree key j={j} ps={page_size} gap={gap_rope}")
         out, lse, err = run_gpu(case)
         assert err == 0
         o = bf16_bits_to_f64(out)
