@@ -901,9 +901,9 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 // grows (O_s = stored fp16 x 2^e_s); empty splits (lse = -inf) are skipped. The
 // waves' states are merged the same way in LDS. out = acc / w rounded to bf16
 // once; lse = M + log2 w in natural-log units.
-// A small grid (one request: a few 32-row blocks x 64 fragment slots) takes
-// 16 waves per workgroup to keep enough loads in flight; a large one 8. Four
-// waves per SIMD either way (two 8-wave workgroups per CU).
+// The waves per workgroup follow NSPLIT (one round of 8 loads per wave where
+// 16 waves allow it), so that a small NSPLIT does not spread one split per
+// wave over workgroups that then wait on a cross-wave merge.
 template <int kCombineWaves>
 __global__ __launch_bounds__(kCombineWaves * 64, 4) void verify_combine_kernel(VerifyLaunch L) {
   __shared__ f32x4 red_acc[kCombineWaves][64];
@@ -1070,10 +1070,20 @@ hipError_t launch_partial(const VerifyLaunch& L, hipStream_t stream) {
 
 hipError_t launch_combine(const VerifyLaunch& L, hipStream_t stream) {
   const int cgrid = L.batch * (L.rows_pad / 32) * 64;
-  if (cgrid <= 512)
+  // Waves per workgroup: enough that a request's NSPLIT splits take one round
+  // of 8 loads per wave (at most 16 waves), and no more: a small NSPLIT gets
+  // small workgroups instead of waves that hold one split each.
+  const int want = (L.nsplit + 7) / 8;
+  if (want > 8)
     hipLaunchKernelGGL(verify_combine_kernel<16>, dim3(cgrid), dim3(16 * 64), 0, stream, L);
-  else
+  else if (want > 4)
     hipLaunchKernelGGL(verify_combine_kernel<8>, dim3(cgrid), dim3(8 * 64), 0, stream, L);
+  else if (want > 2)
+    hipLaunchKernelGGL(verify_combine_kernel<4>, dim3(cgrid), dim3(4 * 64), 0, stream, L);
+  else if (want > 1)
+    hipLaunchKernelGGL(verify_combine_kernel<2>, dim3(cgrid), dim3(2 * 64), 0, stream, L);
+  else
+    hipLaunchKernelGGL(verify_combine_kernel<1>, dim3(cgrid), dim3(64), 0, stream, L);
   return hipGetLastError();
 }
 
