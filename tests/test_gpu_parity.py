@@ -120,14 +120,16 @@ def test_parity_tiny_config(nsplit):
 
 
 def test_parity_4k_config_nsplit_sweep():
-    # One request of 128 rows (one row block): NSPLIT 64, 1 and 7 give grids of
-    # at most a quarter of the CUs (four column parts), 128 half of them (two),
-    # 257 more (one), so every column-part mode meets the oracle here.
+    # One request of 128 rows (one row block): NSPLIT 64, 1, 7 and 16 give
+    # grids of at most a quarter of the CUs (four column parts), 128 half of
+    # them (two), 257 more (one), so every column-part mode meets the oracle
+    # here. The combine's workgroup sizes follow NSPLIT: 1 wave (1, 7), 2 (16),
+    # 8 (64) and 16 (128, 257).
     case = make_case("C2")
     ref = oracle_case(case)
     dc = device_case(case)
     outs = {}
-    for ns in [64, 1, 7, 128, 257]:
+    for ns in [64, 1, 7, 16, 128, 257]:
         say(f"C2 nsplit={ns}")
         out, lse, err = run_gpu(case, nsplit=ns, dc=dc)
         assert err == 0
