@@ -151,6 +151,15 @@ __device__ __forceinline__ void store_agent8(T* p, const T& v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// v, opaque to the compiler from here on: lane-derived addresses computed
+// from it are rebuilt where they are used (one VALU operation) rather than
+// hoisted to the kernel's start and spilled to scratch across the tile loop
+// (each reload would put a memory round trip into the next window's setup).
+__device__ __forceinline__ int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // f(integral_constant<int, 0>{}), ..., f(integral_constant<int, N-1>{}): a
 // loop whose index is a compile-time constant in every copy of the body.
 template <typename F, int... I>
@@ -391,10 +400,11 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     const int npg = ((w0 + wn - 1) >> L.page_shift) - pg0 + 1;
     const int32_t* pt = L.page_table + static_cast<size_t>(b) * L.max_pages + pg0;
     const uint32_t pt_lds = lds_addr(L.page_shift == 0 ? slot_s : pt_s);
+    const int ln = fresh(lane);
     for (int j0 = wid * 64; j0 < npg; j0 += NW * 64)
-      if (j0 + lane < npg) dma4(pt + j0 + lane, pt_lds + j0 * 4);
+      if (j0 + ln < npg) dma4(pt + j0 + ln, pt_lds + j0 * 4);
     const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
-    for (int i = threadIdx.x; i < ntiles; i += NW * 64) badbits_s[i] = 0u;
+    for (int i = fresh(static_cast<int>(threadIdx.x)); i < ntiles; i += NW * 64) badbits_s[i] = 0u;
   };
   request_window(k0, min(k1 - k0, kSlotCap));
 
@@ -642,7 +652,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       // Physical slot of every key in this window; bad slots are recorded in
       // the tile's bad-key bits and loaded from slot 0 instead.
       int bad = 0;
-      for (int i = threadIdx.x; i < wn; i += NW * 64) {
+      for (int i = fresh(static_cast<int>(threadIdx.x)); i < wn; i += NW * 64) {
         const int p = w0 + i;
         const int page = ptab[(p >> L.page_shift) - pg0];
         const int64_t slot = (static_cast<int64_t>(page) << L.page_shift) + (p & ((1 << L.page_shift) - 1));
@@ -658,7 +668,8 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       if (lane == 0) badw_s[wid] = wave_bad;
       if (kMode == kPassAdaptive && need_mask && w0 == k0 && wid == 0) {
         // sparse decode: every node is a root (one query token per request)
-        const uint64_t a = kSparse ? (lane < T ? 1ull << lane : 0ull) : ancestor_bits_of(parent, T, lane, L.err);
+        const int ln = fresh(lane);
+        const uint64_t a = kSparse ? (ln < T ? 1ull << ln : 0ull) : ancestor_bits_of(parent, T, ln, L.err);
         anc_s[lane] = a;
       }
       lds_barrier();
