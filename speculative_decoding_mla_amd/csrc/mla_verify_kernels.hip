@@ -85,7 +85,7 @@ constexpr int kStages = 4;
 constexpr int kSlotCap = 2048;
 constexpr int kQSteps = kQkDim / 16;                               // 36 k-steps of 16
 constexpr int kColBlocks = kVDim / 32;                             // 16
-constexpr float kRefLift = 32.0f;  // log2 units: reference above the first visible tile max
+constexpr float kRefLift = 32.0f;  // log2 units: reference above the max of the split's first tile
 constexpr float kRefHead = 96.0f;  // log2 units: largest weight kept is 2^kRefHead
 constexpr float kHeadWeight = 0x1p96f;  // 2^kRefHead
 
@@ -435,7 +435,6 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   }
 
   bf16x8 qf[kQSteps];  // lane: dims 16ks + 8*hsel + 0..7 of row lane%32
-  const int node = row_ok ? row / L.heads : 0;
   const bool need_mask = k1 > ctx;
   uint64_t my_anc = 0;
 
@@ -670,7 +669,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
         // sparse decode: every node is a root (one query token per request)
         const int ln = fresh(lane);
         const uint64_t a = kSparse ? (ln < T ? 1ull << ln : 0ull) : ancestor_bits_of(parent, T, ln, L.err);
-        anc_s[lane] = a;
+        anc_s[ln] = a;
       }
       lds_barrier();
       if (kMode == kPassAdaptive) {
@@ -678,7 +677,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
 #pragma unroll
         for (int w = 0; w < NW; ++w) win_bad |= badw_s[w] != 0;
         if (win_bad && threadIdx.x == 0) atomicOr(L.err, MLA_DEVERR_SLOT_RANGE);
-        if (need_mask && w0 == k0) my_anc = anc_s[node];
+        if (need_mask && w0 == k0) {
+          const int r = rb * (NW * 32) + wid * 32 + (fresh(lane) & 31);
+          my_anc = anc_s[(r < L.rows ? r : 0) / fresh(L.heads)];  // this lane's node (divisor rebuilt here too)
+        }
       }
 
       // Slots behind this wave's loads of tile t: load i is the latent part of
