@@ -25,7 +25,7 @@ namespace mlav {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -286,52 +286,23 @@ __global__ __launch_bounds__(256) void window_map_kernel(const int32_t* __restri
 
 // ---------------------------------------------------------------- fp8 indexer logits
 
-// Eight E4M3 codes (two dwords) widened exactly to bf16: the hardware
-// conversion gives fp32, and a value with at most four significant bits is a
-// bf16 whose pattern is the fp32 pattern's upper half.
+// Eight E4M3 codes (two dwords) widened exactly to bf16 (four significant
+// bits fit bf16's eight, and the exponent range is wider): one gfx950
+// conversion per pair of codes, with scale 1. The order of the eight values is
+// that of the bytes; any fixed order serves, as queries and keys are widened
+// alike.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  const u32x4v packed = {
-      (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u),
-      (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u),
-      (__float_as_uint(c[0]) >> 16) | (__float_as_uint(c[1]) & 0xffff0000u),
-      (__float_as_uint(d[0]) >> 16) | (__float_as_uint(d[1]) & 0xffff0000u)};
-  return __builtin_bit_cast(bf16x8, packed);
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
+
+// max(x, 0) on the bit pattern: a negative float is a negative int32
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 constexpr int kIdxPage = 64, kIdxDim = 128, kIdxBlockBytes = 8448, kIdxScaleOff = kIdxPage * kIdxDim;
-
-// Sum of v[0..15] over the 32 lanes of each wave half, by halving: at the step
-// with lane bit m, a lane keeps the half of its values its bit selects, and
-// adds the partner's copy of that half (one shuffle per kept value). After the
-// four steps m = 16, 8, 4, 2 a lane holds element 8 b4 + 4 b3 + 2 b2 + b1 (bits
-// of lane % 32) summed over 16 lanes; the step m = 1 completes the 32 lanes.
-// 16 shuffles in all instead of 80.
-__device__ __forceinline__ float head_sum_halving(const float (&v)[16], int lane) {
-  float a8[8], a4[4], a2[2];
-  {
-    const bool up = lane & 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a8[i] = (up ? v[i + 8] : v[i]) + __shfl_xor(up ? v[i] : v[i + 8], 16);
-  }
-  {
-    const bool up = lane & 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a4[i] = (up ? a8[i + 4] : a8[i]) + __shfl_xor(up ? a8[i] : a8[i + 4], 8);
-  }
-  {
-    const bool up = lane & 4;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a2[i] = (up ? a4[i + 2] : a4[i]) + __shfl_xor(up ? a4[i] : a4[i + 2], 4);
-  }
-  const bool up = lane & 2;
-  const float a1 = (up ? a2[1] : a2[0]) + __shfl_xor(up ? a2[0] : a2[1], 2);
-  return a1 + __shfl_xor(a1, 1);
-}
 
 // Persistent waves, independent of each other (no barrier, no LDS): the
 // work unit is half a block, 32 positions x all 64 heads. Wave g of the grid
@@ -339,11 +310,13 @@ __device__ __forceinline__ float head_sum_halving(const float (&v)[16], int lane
 // space: the run's block ids, lengths and requests are read once (one lane per
 // unit), the request's queries are widened to bf16 once and stay in
 // registers, and the next unit's 4 KiB are loaded while the current one is
-// multiplied. A unit is two 32 x 32 tiles of K Q^T (head halves) over the same
+// multiplied. A unit is two 32 x 32 tiles of Q K^T (head halves) over the same
 // K fragments: 16 MFMAs. The contraction index is permuted the same way on
 // both sides (k-step ks and lane half hs cover dims 64 hs + 8 ks + 0..7), so a
-// lane's operand bytes are 64 contiguous bytes of its row. The ReLU, the head
-// weights and the sum over the 64 heads stay in registers (head_sum_halving).
+// lane's operand bytes are 64 contiguous bytes of its row. Heads are the rows
+// of the product and positions its columns, so each lane ends with 32 heads
+// of one position: the ReLU, the head weights and the sum over heads are done
+// in its registers, and one exchange between the lane halves completes it.
 __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
   const int lane = threadIdx.x & 63;
   const int hs = lane >> 5;
@@ -356,87 +329,126 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
   const int cnt = min(units, first + per) - first;
   if (cnt <= 0) return;
 
+  const int hd = lane & 31;  // this lane's query row in each head half, and its key row
+
+  // The product's rows held by this lane: heads 32 h2 + wrow(j), j = 0..15.
+  auto wrow = [&](int j) { return 8 * (j >> 2) + 4 * hs + (j & 3); };
+  // The queries of a request, as stored (widened later), and the weights of
+  // the heads this lane sums: lane (hs, hd) holds bytes 64 hs .. 64 hs + 63
+  // of head hd and of head 32 + hd. Heads past the count are read as head 0
+  // and zeroed at widening.
+  u32x4 qraw[2][4];
+  float wv[2][16];
+  auto load_q = [&](int b) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int head = h2 * 32 + hd < I.heads ? h2 * 32 + hd : 0;
+      const u32x4* qrow =
+          reinterpret_cast<const u32x4*>(I.q + (static_cast<size_t>(b) * I.heads + head) * kIdxDim + hs * 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qraw[h2][i] = qrow[i];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int hw = h2 * 32 + wrow(j);
+        wv[h2][j] = I.weights[static_cast<size_t>(b) * I.heads + (hw < I.heads ? hw : 0)];
+      }
+    }
+  };
+  // The run's first request is known from the unit index alone: its queries
+  // are requested before anything else, so they arrive first.
+  load_q(first / (2 * I.max_blocks));
+
   // lane k < cnt describes unit `first + k`: request, clamped length, block id
-  // (-1 past the length, -2 out of range)
-  // The table entry is read together with the length (the table is in bounds
-  // whatever the length; an entry past it is never used), so the block ids
-  // are one round trip away, not two.
-  int my_b = 0, my_n = 0, my_blk = -1;
-  if (lane < cnt) {
-    const int u = first + lane;
+  // (-1 past the length, -2 out of range); lanes past the run repeat the last
+  // unit's reads (every lane loads, so the number of loads in flight is fixed)
+  // and describe nothing. The table entry is read together with the length
+  // (the table is in bounds whatever the length; an entry past it is never
+  // used), so the block ids are one round trip away, not two.
+  int my_b, my_n, my_blk = -1;
+  {
+    const int u = first + min(lane, cnt - 1);
     my_b = u / (2 * I.max_blocks);
     const int page = (u >> 1) - my_b * I.max_blocks;
-    const int raw = I.seq_lens[my_b];
-    const int entry = I.block_table[u >> 1];
+    int raw = I.seq_lens[my_b];
+    int entry = I.block_table[u >> 1];
+    asm volatile("" : "+v"(raw), "+v"(entry));  // both reads issued before either is waited for
     my_n = min(max(raw, 0), cap);
-    if (raw != my_n && page == 0 && (u & 1) == 0) flag(I.err, MLA_DEVERR_SEQ_LEN);
-    if (page * kIdxPage + (u & 1) * 32 < my_n) {
-      my_blk = entry;
-      if (my_blk < 0 || my_blk >= I.num_blocks) {
-        flag(I.err, MLA_DEVERR_SLOT_RANGE);
-        my_blk = -2;
+    if (lane < cnt) {
+      if (raw != my_n && page == 0 && (u & 1) == 0) flag(I.err, MLA_DEVERR_SEQ_LEN);
+      if (page * kIdxPage + (u & 1) * 32 < my_n) {
+        my_blk = entry;
+        if (my_blk < 0 || my_blk >= I.num_blocks) {
+          flag(I.err, MLA_DEVERR_SLOT_RANGE);
+          my_blk = -2;
+        }
       }
     }
   }
 
-  const int hd = lane & 31;  // this lane's head in each half, and its row of the K tile
-  // the position whose head sum this lane ends up holding (head_sum_halving)
-  const int j_sum = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
-  const int r_sum = 8 * (j_sum >> 2) + 4 * hs + (j_sum & 3);
   // A unit's bytes (this lane's 64 bytes of the K tile, and the scale of the
   // position it will hold) are loaded kAhead units before they are used;
   // loads retire in issue order, so nothing that waits on a unit's bytes also
-  // waits on a later unit's.
+  // waits on a later unit's. The loads are issued for every unit, also past
+  // the run or the length (then from block 0, which always exists, and never
+  // used): with a load count that does not depend on the data, each wait
+  // counts exactly the loads issued after its unit. Loads under a condition
+  // make every later wait assume the fewest loads, which drains the prefetch.
   constexpr int kAhead = 2;
   struct UnitBytes {
     u32x4 k[4];
     float scale;
   };
   auto load_unit = [&](int kk, UnitBytes& dst) {
-    const int blk = __shfl(my_blk, kk);
-    if (kk < cnt && blk >= 0) {
-      const uint8_t* block = I.kv_blocks + static_cast<size_t>(blk) * kIdxBlockBytes;
-      const int half = (first + kk) & 1;
-      dst.scale = reinterpret_cast<const float*>(block + kIdxScaleOff)[half * 32 + r_sum];
-      const u32x4* a = reinterpret_cast<const u32x4*>(block + (half * 32 + hd) * kIdxDim + hs * 64);
+    const int blk = __shfl(my_blk, kk & 63);
+    const int use = kk < cnt && blk >= 0 ? blk : 0;
+    const uint8_t* block = I.kv_blocks + static_cast<size_t>(use) * kIdxBlockBytes;
+    const int half = (first + kk) & 1;
+    dst.scale = reinterpret_cast<const float*>(block + kIdxScaleOff)[half * 32 + hd];
+    const u32x4* a = reinterpret_cast<const u32x4*>(block + (half * 32 + hd) * kIdxDim + hs * 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst.k[i] = a[i];
-    }
+    for (int i = 0; i < 4; ++i) dst.k[i] = a[i];
   };
 
-  int cur_b = -1;
   bf16x8 q0[8], q1[8];
-  float w0 = 0.f, w1 = 0.f;
+  auto widen_q = [&]() {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bool ok = h2 * 32 + hd < I.heads;
+      bf16x8(&qd)[8] = h2 == 0 ? q0 : q1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 qq = ok ? qraw[h2][i] : u32x4{0u, 0u, 0u, 0u};
+        qd[2 * i] = e4m3x8_to_bf16(qq[0], qq[1]);
+        qd[2 * i + 1] = e4m3x8_to_bf16(qq[2], qq[3]);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (h2 * 32 + wrow(j) >= I.heads) wv[h2][j] = 0.f;
+    }
+  };
+  int cur_b = first / (2 * I.max_blocks);
   auto process = [&](int kk, const UnitBytes& ub) {
     const int u = first + kk;
-    const int b = __shfl(my_b, kk);
-    const int n = __shfl(my_n, kk);
-    const int blk = __shfl(my_blk, kk);
+    const int b = __shfl(my_b, kk & 63);
+    const int n = __shfl(my_n, kk & 63);
+    const int blk = __shfl(my_blk, kk & 63);
     const int page = (u >> 1) - b * I.max_blocks;
     const int pos0 = page * kIdxPage + (u & 1) * 32;
     float* out = I.logits + static_cast<size_t>(b) * cap + pos0;
-    if (blk < 0) {  // past the length, or an out-of-range block: nothing to read
-      if (lane < 32) out[lane] = -INFINITY;
+    if (kk >= cnt || blk < 0) {
+      // Past the run (nothing to write), past the length or an out-of-range
+      // block (-inf): the unit's bytes are not used, but are waited for here as
+      // on the other path, so that no later wait has to allow for them.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(ub.k[i]));
+      asm volatile("" ::"v"(ub.scale));
+      if (kk < cnt && lane < 32) out[lane] = -INFINITY;
       return;
     }
-    if (b != cur_b) {  // a new request: its queries (widened once) and head weights
+    if (b != cur_b) {  // a new request within the run: its queries and head weights
       cur_b = b;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int head = h2 * 32 + hd;
-        const bool ok = head < I.heads;
-        const u32x4* qrow = reinterpret_cast<const u32x4*>(
-            I.q + (static_cast<size_t>(b) * I.heads + (ok ? head : 0)) * kIdxDim + hs * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 qq = ok ? qrow[i] : u32x4{0u, 0u, 0u, 0u};
-          bf16x8(&qd)[8] = h2 == 0 ? q0 : q1;
-          qd[2 * i] = e4m3x8_to_bf16(qq[0], qq[1]);
-          qd[2 * i + 1] = e4m3x8_to_bf16(qq[2], qq[3]);
-        }
-        const float wv = ok ? I.weights[static_cast<size_t>(b) * I.heads + head] : 0.f;
-        if (h2 == 0) w0 = wv; else w1 = wv;
-      }
+      load_q(b);
+      widen_q();
     }
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -444,28 +456,41 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
       const u32x4& a = ub.k[ks >> 1];
       const int o = (ks & 1) * 2;
       const bf16x8 kb = e4m3x8_to_bf16(a[o], a[o + 1]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, q0[ks], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, q1[ks], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0[ks], kb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1[ks], kb, acc1, 0, 0, 0);
     }
-    // lane holds C[r][head] for r = 8 (j / 4) + 4 hs + j % 4 in both head halves
-    float v[16];
+    // lane holds the products of position hd with heads wrow(j) (acc0) and
+    // 32 + wrow(j) (acc1); four partial sums keep the chain of adds short
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = w0 * fmaxf(acc0[j], 0.f) + w1 * fmaxf(acc1[j], 0.f);
-    const float sum = head_sum_halving(v, lane);
-    if ((lane & 1) == 0) out[r_sum] = pos0 + r_sum < n ? sum * ub.scale : -INFINITY;
+    for (int j = 0; j < 16; ++j) {
+      part[j & 3] = fmaf(wv[0][j], relu_bits(acc0[j]), part[j & 3]);
+      part[j & 3] = fmaf(wv[1][j], relu_bits(acc1[j]), part[j & 3]);
+    }
+    float sum = (part[0] + part[1]) + (part[2] + part[3]);
+    sum += __shfl_xor(sum, 32);  // the other lane half's 32 heads
+    if (lane < 32) out[hd] = pos0 + hd < n ? sum * ub.scale : -INFINITY;
   };
 
   // ring of kAhead + 1 units, unrolled so that every ring index is a constant
   UnitBytes ring[kAhead + 1];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) load_unit(i, ring[i]);
+  // the first request's queries are widened while the first units are in
+  // flight (the empty statements keep the widening after the loads' issue)
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(qraw[h2][i])::"memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(wv[h2][j])::"memory");
+  }
+  widen_q();
   for (int k = 0; k < cnt; k += kAhead + 1) {
 #pragma unroll
     for (int slot = 0; slot <= kAhead; ++slot) {
-      if (k + slot < cnt) {
-        load_unit(k + slot + kAhead, ring[(slot + kAhead) % (kAhead + 1)]);
-        process(k + slot, ring[slot]);
-      }
+      load_unit(k + slot + kAhead, ring[(slot + kAhead) % (kAhead + 1)]);
+      process(k + slot, ring[slot]);
     }
   }
 }
