@@ -30,7 +30,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowChunks = 72;  // 16-byte chunks of a 1,152-byte latent row
-constexpr int kIndexerGrid = 512;  // persistent indexer workgroups: two per CU (two waves per SIMD at 142 VGPRs)
+// Persistent indexer workgroups: one per CU, one wave per SIMD. Measured
+// against two per CU (two waves per SIMD fit the registers): fewer, longer
+// runs are faster, as each run pays two dependent round trips (block table,
+// then keys) before its stream starts.
+constexpr int kIndexerGrid = 256;
 
 __device__ __forceinline__ void flag(uint32_t* err, uint32_t bit) {
   if (err != nullptr) atomicOr(err, bit);
@@ -389,8 +393,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
   // position it will hold) are loaded kAhead units before they are used;
   // loads retire in issue order, so nothing that waits on a unit's bytes also
   // waits on a later unit's. The loads are issued for every unit, also past
-  // the run or the length (then from block 0, which always exists, and never
-  // used): with a load count that does not depend on the data, each wait
+  // the run or the length (then from a block that exists, and never used):
+  // with a load count that does not depend on the data, each wait
   // counts exactly the loads issued after its unit. Loads under a condition
   // make every later wait assume the fewest loads, which drains the prefetch.
   constexpr int kAhead = 2;
@@ -398,9 +402,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch I) {
     u32x4 k[4];
     float scale;
   };
+  // Units past the run or the length read the run's last block instead (in
+  // this wave's cache already; one block shared by every wave would be a hot
+  // spot), or block 0 when that one is past the length too.
+  const int spare_blk = max(__shfl(my_blk, cnt - 1), 0);
   auto load_unit = [&](int kk, UnitBytes& dst) {
     const int blk = __shfl(my_blk, kk & 63);
-    const int use = kk < cnt && blk >= 0 ? blk : 0;
+    const int use = kk < cnt && blk >= 0 ? blk : spare_blk;
     const uint8_t* block = I.kv_blocks + static_cast<size_t>(use) * kIdxBlockBytes;
     const int half = (first + kk) & 1;
     dst.scale = reinterpret_cast<const float*>(block + kIdxScaleOff)[half * 32 + hd];
