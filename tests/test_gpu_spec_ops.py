@@ -402,6 +402,22 @@ def test_indexer_full_table():
     check_indexer(c, got, "full table")
 
 
+def test_indexer_runs_cross_requests():
+    """Persistent waves take runs of consecutive half-blocks (at least 1,024
+    waves): 3 x 701 blocks = 4,206 half-blocks give runs of 5 that start and
+    end inside requests (1,402 and 2,804 are not multiples of 5), so a wave
+    switches requests mid-run, after half-blocks past a length, and with
+    48 heads (rows past the count are zero)."""
+    c = indexer_case(707, batch=3, heads=48, max_blocks=701, seq_lens=[44_800, 44_864, 3_001])
+    units = 3 * 701 * 2
+    per = -(-units // 1024)
+    assert per > 3 and (701 * 2) % per != 0 and (2 * 701 * 2) % per != 0
+    say("indexer runs across requests")
+    got, err = run_indexer(c)
+    assert err == 0
+    check_indexer(c, got, "runs across requests")
+
+
 def test_indexer_bad_block_flagged():
     c = indexer_case(706, batch=1, heads=64, max_blocks=4, seq_lens=[256])
     bt = c.block_table.copy()
