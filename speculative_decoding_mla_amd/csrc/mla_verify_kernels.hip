@@ -88,6 +88,7 @@ constexpr int kColBlocks = kVDim / 32;                             // 16
 constexpr float kRefLift = 32.0f;  // log2 units: reference above the max of the split's first tile
 constexpr float kRefHead = 96.0f;  // log2 units: largest weight kept is 2^kRefHead
 constexpr float kHeadWeight = 0x1p96f;  // 2^kRefHead
+static_assert(kRefHead == 96.0f, "kHeadWeight must stay 2^kRefHead");
 
 // 16-byte chunk permutation inside a 128-byte group, keyed by the key's index
 // in the tile: 8 consecutive keys hit 8 distinct slots (K reads), and the
