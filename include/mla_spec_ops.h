@@ -188,9 +188,9 @@ MLA_API mla_status mla_window_map(const int32_t* target_map, int32_t map_stride,
  * "Design Decisions and Assumptions": the DSA indexer scores every cached
  * position of a request: q . k per head, ReLU, times a per-head weight, summed
  * over heads, times the position's scale. The cache is paged in blocks of
- * 8,448 bytes: 64 positions x 128 fp8 E4M3 values, then 64 fp32 scales. One
- * workgroup per (request, block) over a fixed grid; blocks past a request's
- * length only write -inf, so the work follows the actual length.
+ * 8,448 bytes: 64 positions x 128 fp8 E4M3 values, then 64 fp32 scales. A
+ * fixed grid of persistent waves streams runs of half-blocks; blocks past a
+ * request's length are not read and only get -inf.
  *   logits[b][p] = ( sum_h weights[b][h] * max(0, q[b,h,:] . k_p) ) * scale_p
  * for p < seq_lens[b], with k_p row p % 64 of block block_table[b][p / 64]
  * (E4M3, OCP form, no separate query scale); -inf for p in [seq_lens[b],
