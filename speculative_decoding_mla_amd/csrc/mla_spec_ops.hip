@@ -313,8 +313,8 @@ constexpr int kIdxPage = 64, kIdxDim = 128, kIdxBlockBytes = 8448, kIdxScaleOff 
 // streams a contiguous run of units of the flattened (request, block, half)
 // space: the run's block ids, lengths and requests are read once (one lane per
 // unit), the request's queries are widened to bf16 once and stay in
-// registers, and the next unit's 4 KiB are loaded while the current one is
-// multiplied. A unit is two 32 x 32 tiles of Q K^T (head halves) over the same
+// registers, and the 4 KiB of the next two units are in flight while the
+// current one is multiplied. A unit is two 32 x 32 tiles of Q K^T (head halves) over the same
 // K fragments: 16 MFMAs. The contraction index is permuted the same way on
 // both sides (k-step ks and lane half hs cover dims 64 hs + 8 ks + 0..7), so a
 // lane's operand bytes are 64 contiguous bytes of its row. Heads are the rows
