@@ -2,18 +2,23 @@
 """Verify-attention benchmark on one MI355X: verify-step latency and effective
 KV bandwidth (fraction of the HBM roofline) against context length.
 
-A step is one verify call: the ancestor mask, the split-KV partial attention
-and the log-sum-exp merge, over one batch of synthetic input. Inputs are in
-HBM before the timed region starts. To measure HBM rather than the 256 MB
-Infinity Cache, the steps cycle over R replicas of the workload whose KV rows
-sit in disjoint regions of one pool (R x KV bytes >= 1 GiB); every replica
-holds the same logical rows, so every step computes the same result. The R
-calls are captured in one hipGraph and replayed.
+A step is one verify call: the split-KV partial attention (which builds the
+ancestor masks in registers) and the log-sum-exp merge, over one batch of
+synthetic input. Inputs are in HBM before the timed region starts. To measure
+HBM rather than the 256 MB Infinity Cache, the steps cycle over R replicas of
+the workload whose KV rows sit in disjoint regions of one pool (R x KV bytes >=
+1 GiB); every replica holds the same logical rows, so every step computes the
+same result. Whole cycles of calls are captured in hipGraphs; the warmup
+replays whole cycles and the timed calls start right after one, so each timed
+call reads a replica last touched R-1 calls earlier.
+
+The default workload is C4a (context 184,728, 32-node tree, 8 heads, page size
+1, fragmented), the largest single-GPU configuration.
 
 Prints one JSON line. Options: --workload (C1, C2, C3, C4a, C4b, C5, a sweep
 point S<context>_T<nodes>[_contig], or one of the rows next to verify, F1_* to
 F4_*), --nsplit, --steps, --warmup, --no-sweep, --full-sweep, --no-cpu,
---no-next.
+--cpu-seconds, --no-next.
 
 The default line also carries next_rows: the steps next to verify (sparse
 top-k decode, KV append + tree accept + commit, the sliding-window slot map,
@@ -44,7 +49,11 @@ QK_DIM, V_DIM = 576, 512
 KV_ROW_BYTES = QK_DIM * 2  # one bf16 latent row per key
 ROTATE_BYTES = 1 << 30     # >= 4 x the 256 MB Infinity Cache
 KERNEL_SOURCE = os.path.join(ROOT, "speculative_decoding_mla_amd", "csrc", "mla_verify_kernels.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "verify_partial_C2_hbm_traffic.md")
+
+def traffic_profile(workload: str) -> str:
+    """The committed counter summary of the partial kernel on a workload."""
+    return os.path.join(ROOT, "profiles", f"verify_partial_{workload}_hbm_traffic.md")
+
 OPS_SOURCE = os.path.join(ROOT, "speculative_decoding_mla_amd", "csrc", "mla_spec_ops.hip")
 INDEXER_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "indexer_F3_B1_262208_hbm_traffic.md")
 # Context-sweep grid (contexts x tree sizes); --full-sweep adds the short contexts.
@@ -121,11 +130,12 @@ def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str, profile: str = TRAFFIC_PROFILE, source: str = KERNEL_SOURCE):
+def measured_traffic(workload: str, profile: str | None = None, source: str = KERNEL_SOURCE):
     """HBM bytes per launch of a kernel from a committed counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel calibration).
     Returns None unless the summary was taken on this workload from the kernel
     source as it is now."""
+    profile = profile or traffic_profile(workload)
     try:
         with open(profile) as f:
             fields = dict(ln.split(":", 1) for ln in f if ln.startswith(("traffic_", "kernel_source_sha256", "workload")))
@@ -237,17 +247,45 @@ def capture(torch, fns):
     return g
 
 
-def run_steps(torch, g_full, per_graph, g_rem, rem, steps):
-    n_full = steps // per_graph
-    for _ in range(n_full):
-        g_full.replay()
-    if rem:
+def cycle_calls(replicas: int) -> int:
+    """Calls per captured graph: whole cycles over the replicas, at least 64
+    calls, so that a small replica count does not add a graph launch per call."""
+    return replicas * max(1, -(-64 // replicas))
+
+
+def time_rotating(torch, make_call, replicas, steps, warmup):
+    """Device time of exactly `steps` calls that cycle over the replicas
+    (call i reads replica i mod R), as ms per call.
+
+    Every graph is captured first (capture runs each call once, eagerly). The
+    warmup then replays whole cycles (at least `warmup` calls, ending on
+    replica R-1), and the timed calls start at replica 0. So every timed call,
+    however few there are, reads a replica last touched R-1 calls earlier: R-1
+    other replicas (>= 1 GiB - one replica's KV) went through the 256 MB
+    Infinity Cache in between, and its rows come from HBM."""
+    per = cycle_calls(replicas)
+    g_cycle = capture(torch, [make_call(i % replicas) for i in range(per)])
+    rem = steps % per
+    g_rem = capture(torch, [make_call(i % replicas) for i in range(rem)]) if rem else None
+    warm_cycles = max(1, -(-warmup // per))
+    for _ in range(warm_cycles):
+        g_cycle.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps // per):
+        g_cycle.replay()
+    if g_rem is not None:
         g_rem.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, warm_cycles * per
 
 
 def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, steps, warmup):
     """Returns (ms per step over exactly `steps` steps, partial-kernel us per
-    launch, out, lse, workspace)."""
+    launch, out, lse, workspace, warmup calls run)."""
     b = rep.q.shape[0]
     out = torch.empty((b, nodes, heads, V_DIM), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((b, nodes, heads), dtype=torch.float32, device="cuda")
@@ -265,44 +303,15 @@ def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, st
                                          ws)
 
     R = rep.replicas
-    # At least 64 calls per graph (cycling over the replicas), so that a small
-    # R does not add a graph launch per call.
-    per_graph = min(max(R, 64), steps)
-    g_full = capture(torch, [full_call(r % R) for r in range(per_graph)])
-    rem = steps % per_graph
-    g_rem = capture(torch, [full_call(r % R) for r in range(rem)]) if rem else None
-    # warmup: W untimed steps
-    w_graph = min(max(R, 64), max(warmup, 1))
-    g_w = capture(torch, [full_call(r % R) for r in range(w_graph)])
-    for _ in range(max(1, warmup // w_graph)):
-        g_w.replay()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    run_steps(torch, g_full, per_graph, g_rem, rem, steps)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / steps
-
-    # the dominant kernel alone, timed with events on the stream it runs on
-    n_p = max(R, 64)
-    g_p = capture(torch, [partial_call(r % R) for r in range(n_p)])
-    g_p.replay()
-    torch.cuda.synchronize()
-    reps = max(1, min(50, (steps + n_p - 1) // n_p))
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g_p.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    partial_us = e0.elapsed_time(e1) * 1e3 / (reps * n_p)
+    ms_per_step, warm_calls = time_rotating(torch, full_call, R, steps, warmup)
+    # the dominant kernel alone, timed the same way with events on the stream
+    # it runs on (at least one whole cycle of calls)
+    p_steps = max(steps, cycle_calls(R))
+    ms_partial, _ = time_rotating(torch, partial_call, R, p_steps, warmup)
     # leave the full result of replica 0 in out/lse
     full_call(0)()
     torch.cuda.synchronize()
-    return ms_per_step, partial_us, out, lse, ws
+    return ms_per_step, ms_partial * 1e3, out, lse, ws, warm_calls
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -601,40 +610,59 @@ def measure_case(torch, mv, case, nsplit, steps, warmup, seed, replicas=None):
     return res, rep
 
 
-def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None, layout="scattered"):
-    """A context-sweep point generated on the GPU (seeded): N(0,1) bf16 rows,
-    uniform-parent tree (depth <= 8 for 32 nodes), page size 1, KV rows
-    scattered over the pool or contiguous."""
-    from workloads.gen import tree_depth_capped, tree_uniform
+def parity_of(case, out_bits, lse, ref=None):
+    """Max-abs error of the GPU result against the oracle (the checker's leg)."""
+    from oracle import bf16_bits_to_f64, oracle_case
+    ref_out, ref_lse = oracle_case(case) if ref is None else ref
+    return dict(out_max_abs=float(np.abs(bf16_bits_to_f64(out_bits) - ref_out).max()),
+                lse_max_abs=float(np.abs(lse.astype(np.float64) - ref_lse).max()),
+                within_tolerance=bool(np.abs(bf16_bits_to_f64(out_bits) - ref_out).max() <= 1e-2 and
+                                      np.abs(lse.astype(np.float64) - ref_lse).max() <= 1e-3))
 
-    rng = np.random.default_rng(seed + context + nodes)
-    tree = tree_depth_capped(nodes, 8, rng) if nodes == 32 else tree_uniform(nodes, rng)
+
+def roofline_fields(seq_lens, nodes, heads, page_size, partial_us):
+    """The partial kernel against both roofs: algorithmic bytes and flops per
+    launch over its measured launch time. `bound` names the roof its
+    arithmetic intensity puts it under."""
+    pbytes = partial_algorithmic_bytes(seq_lens, nodes, heads, page_size)
+    pflops = algorithmic_flops(seq_lens, nodes, heads)
+    gbs = pbytes / (partial_us * 1e-6) / 1e9
+    tflops = pflops / (partial_us * 1e-6) / 1e12
+    return dict(bound=roof_bound(nodes, heads), bytes_per_launch=pbytes, flops_per_launch=pflops,
+                achieved_gbs=gbs, achieved_tflops=tflops, hbm_frac=gbs / HBM_PEAK_GBS,
+                mfma_frac=tflops / BF16_PEAK_TFLOPS)
+
+
+def sweep_point(torch, mv, context, nodes, heads=8, nsplit=None, layout="scattered", with_parity=True):
+    """A context-sweep point: the seeded sweep case (N(0,1) bf16 rows and
+    queries, uniform-parent tree, depth <= 8 for 32 nodes, page size 1), its
+    logical rows replicated over a >= 1 GiB pool, scattered or contiguous;
+    parity of the result against the oracle."""
+    from workloads import sweep_case
+
     n = context + nodes
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(seed * 1000 + nodes)
-    rows = torch.randn((n, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    q = torch.randn((1, nodes, heads, QK_DIM), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    kvb = kv_bytes([n])
-    replicas = max(1, math.ceil(ROTATE_BYTES / kvb))
-    rep = Replicated(torch, rows, q, [n], tree[None, :], 1, replicas, seed, layout=layout)
-    del rows
     nsplit = nsplit or default_nsplit(1, nodes, heads, n)
-    steps = replicas * max(2, 64 // replicas)
-    ms, partial_us, *_ = time_workload(torch, mv, rep, nodes, heads, nsplit, 1.0 / math.sqrt(192.0), steps,
-                                       replicas)
+    case = sweep_case(context, nodes, nsplit=nsplit)
+    rows = bf16_from_bits(torch, logical_rows_of_case(case)).cuda()
+    q = bf16_from_bits(torch, case.q).cuda()
+    replicas = max(1, math.ceil(ROTATE_BYTES / kv_bytes([n])))
+    rep = Replicated(torch, rows, q, case.seq_lens, case.tree_parent, 1, replicas, 7, layout=layout)
+    del rows
+    steps = cycle_calls(replicas) * 2
+    ms, partial_us, out, lse, *_ = time_workload(torch, mv, rep, nodes, heads, nsplit, case.sm_scale, steps,
+                                                 replicas)
     lat_us = ms * 1e3
     eff = effective_kv_gbs([n], lat_us * 1e-6)
-    pbytes = partial_algorithmic_bytes([n], nodes, heads, 1)
-    flops = algorithmic_flops([n], nodes, heads)
+    rf = roofline_fields([n], nodes, heads, 1, partial_us)
     entry = dict(workload=f"context {context}, {nodes}-node tree, {heads} heads, page size 1, {layout} KV rows",
-                 layout=layout,
-                 context=context, nodes=nodes, rows=nodes * heads, nsplit=nsplit, replicas=replicas,
+                 layout=layout, context=context, nodes=nodes, rows=nodes * heads, nsplit=nsplit, replicas=replicas,
                  latency_us=round(lat_us, 2), eff_kv_gbs=round(eff, 1), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
-                 partial_us=round(partial_us, 2),
-                 partial_hbm_frac=round(pbytes / (partial_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                 partial_mfma_frac=round(flops / (partial_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                 bound=roof_bound(nodes, heads))
-    del rep
+                 partial_us=round(partial_us, 2), partial_hbm_frac=round(rf["hbm_frac"], 4),
+                 partial_mfma_frac=round(rf["mfma_frac"], 4), bound=rf["bound"])
+    if with_parity:
+        entry["parity_vs_oracle"] = parity_of(case, out.view(torch.int16).cpu().numpy().view(np.uint16),
+                                              lse.cpu().numpy())
+    del rep, out, lse
     torch.cuda.empty_cache()
     return entry
 
@@ -642,15 +670,16 @@ def sweep_point(torch, mv, context, nodes, heads=8, seed=7, nsplit=None, layout=
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2048)
-    ap.add_argument("--warmup", type=int, default=256)
-    ap.add_argument("--workload", default="C2",
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="C4a",
                     help="C1, C2, C3, C4a, C4b, C5, a context-sweep point S<context>_T<nodes>[_contig], or one "
                          "row next to verify: " + ", ".join(NEXT_ROWS))
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--full-sweep", action="store_true", help="contexts from 1k to 184,728 (27 points)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="host time budget of the oracle baseline")
     ap.add_argument("--no-next", action="store_true", help="skip the rows next to verify (sparse decode, accept/"
                                                             "commit, window map, fp8 indexer)")
     ap.add_argument("--seed", type=int, default=1234)
@@ -675,7 +704,7 @@ def main():
         spec = args.workload[1:].split("_")
         ctx, nodes = int(spec[0]), int(spec[1][1:])
         layout = "contiguous" if spec[2:] == ["contig"] else "scattered"
-        e = sweep_point(torch, mv, ctx, nodes, nsplit=args.nsplit, layout=layout)
+        e = sweep_point(torch, mv, ctx, nodes, nsplit=args.nsplit, layout=layout, with_parity=not args.no_cpu)
         log(json.dumps(e))
         print(json.dumps(dict(metric=METRIC, value=e["eff_kv_gbs"], unit="GB/s", n_gpus=1, latency_us=e["latency_us"],
                               config=dict(workload=e["workload"]), sweep=[e])), flush=True)
@@ -686,29 +715,31 @@ def main():
     case = make_case(args.workload, nsplit=args.nsplit)
     log(f"timing {args.workload}: {args.steps} steps after {args.warmup} warmup")
     nsplit = case.nsplit
-    (ms, partial_us, out, lse, ws), rep = measure_case(torch, mv, case, nsplit, args.steps, args.warmup,
-                                                        args.seed)
+    (ms, partial_us, out, lse, ws, warm_calls), rep = measure_case(torch, mv, case, nsplit, args.steps,
+                                                                    args.warmup, args.seed)
     dev_err = mv.device_error(ws)
     lat_us = ms * 1e3
     kvb = kv_bytes(case.seq_lens)
     eff = effective_kv_gbs(case.seq_lens, lat_us * 1e-6)
-    bound = roof_bound(case.num_nodes, case.num_heads)
-    pbytes = partial_algorithmic_bytes(case.seq_lens, case.num_nodes, case.num_heads, case.page_size)
-    pflops = algorithmic_flops(case.seq_lens, case.num_nodes, case.num_heads)
+    rf = roofline_fields(case.seq_lens, case.num_nodes, case.num_heads, case.page_size, partial_us)
     traffic = measured_traffic(args.workload)
-    if bound == "hbm":
-        achieved = pbytes / (partial_us * 1e-6) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
+    if rf["bound"] == "hbm":
+        roof = dict(bound="hbm", achieved=round(rf["achieved_gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(rf["hbm_frac"], 4), traffic=traffic)
     else:
-        achieved = pflops / (partial_us * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=traffic)
-    roof.update(kernel="verify_partial_kernel", kernel_us=round(partial_us, 3), bytes_per_launch=pbytes,
-                flops_per_launch=pflops)
+        roof = dict(bound="mfma", achieved=round(rf["achieved_tflops"], 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(rf["mfma_frac"], 4), traffic=traffic)
+    # both roofs side by side, whichever binds
+    roof.update(kernel="verify_partial_kernel", kernel_us=round(partial_us, 3), bytes_per_launch=rf["bytes_per_launch"],
+                flops_per_launch=rf["flops_per_launch"], hbm_gbs=round(rf["achieved_gbs"], 1),
+                hbm_frac=round(rf["hbm_frac"], 4), mfma_tflops=round(rf["achieved_tflops"], 1),
+                mfma_frac=round(rf["mfma_frac"], 4))
+    if traffic:
+        roof["traffic_over_algorithmic"] = round(traffic / rf["bytes_per_launch"], 3)
     gpu_out = out.view(torch.int16).cpu().numpy().view(np.uint16)
     gpu_lse = lse.cpu().numpy()
     layout = rep.layout
+    replicas = rep.replicas
     del rep, out, lse, ws
     torch.cuda.empty_cache()
 
@@ -718,16 +749,19 @@ def main():
                 config=dict(workload=f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
                             context=case.meta["context"], nodes=case.num_nodes, heads=case.num_heads,
                             page_size=case.page_size, nsplit=nsplit, rows=case.num_nodes * case.num_heads,
-                            replicas=math.ceil(ROTATE_BYTES / kvb), layout=layout,
-                            parallelism="none (1 GPU)"),
+                            replicas=replicas, layout=layout, parallelism="none (1 GPU)"),
                 latency_us=round(lat_us, 3), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
-                roofline=roof, device_error=dev_err)
+                roofline=roof, device_error=dev_err,
+                timing=dict(warmup_calls_run=warm_calls,
+                            rotation=f"{replicas} replicas of the workload's KV (>= 1 GiB together); timed calls "
+                                     "cycle over them starting right after a whole warmup cycle, so each reads "
+                                     "a replica last touched R-1 calls earlier"))
 
     log(f"{args.workload}: {lat_us:.2f} us/step, partial kernel {partial_us:.2f} us")
     # The same workload from one replica: its KV stays in the 256 MB Infinity
     # Cache between steps. Reported beside the rotating-replica number, which
     # is the measurement; this one is labelled cache-resident.
-    (w_ms, w_partial_us, *_), w_rep = measure_case(torch, mv, case, nsplit, 512, 64, args.seed, replicas=1)
+    (w_ms, w_partial_us, *_), w_rep = measure_case(torch, mv, case, nsplit, 256, 64, args.seed, replicas=1)
     del w_rep
     torch.cuda.empty_cache()
     line["warm_cache_resident"] = dict(latency_us=round(w_ms * 1e3, 3), partial_us=round(w_partial_us, 3),
@@ -745,18 +779,17 @@ def main():
             line["eff_kv_frac_of_measured_read"] = round(eff / peaks["hbm_read_gbs"], 4)
     if not args.no_cpu:
         log("timing the CPU oracle")
-        med, reps, threads, ref = cpu_baseline(case)
+        budget = args.cpu_seconds
+        med, reps, threads, ref = cpu_baseline(case, budget_s=budget)
         line["cpu_baseline"] = dict(value=round(kvb / med / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
-                                    sample=f"whole {args.workload} verify call, {reps} timed runs, median "
+                                    sample=f"the whole {args.workload} verify call (all {kvb // KV_ROW_BYTES} keys), "
+                                           f"{reps} timed run(s) in a {budget:.0f} s budget, median "
                                            f"{med * 1e6:.0f} us; CPU {cpu_model()}")
-        med1, reps1 = cpu_baseline_one_thread(case)
+        med1, reps1 = cpu_baseline_one_thread(case, budget_s=budget, max_reps=3)
         line["cpu_baseline_1thread"] = dict(value=round(kvb / med1 / 1e9, 4), unit="GB/s", cores=1,
-                                            kind="oracle", sample=f"the same call, {reps1} timed runs, median "
+                                            kind="oracle", sample=f"the same call, {reps1} timed run(s), median "
                                                                   f"{med1 * 1e6:.0f} us, BLAS limited to 1 thread")
-        from oracle import bf16_bits_to_f64
-        o = bf16_bits_to_f64(gpu_out)
-        line["parity_vs_oracle"] = dict(out_max_abs=float(np.abs(o - ref[0]).max()),
-                                        lse_max_abs=float(np.abs(gpu_lse - ref[1]).max()))
+        line["parity_vs_oracle"] = parity_of(case, gpu_out, gpu_lse, ref=ref)
 
     if not args.no_next:
         line["next_rows"] = measure_next_rows(torch, mv, with_cpu=not args.no_cpu)
@@ -764,7 +797,7 @@ def main():
     if not args.no_sweep:
         sweep = []
         for ctx, t in (FULL_SWEEP if args.full_sweep else SWEEP):
-            sweep.append(sweep_point(torch, mv, ctx, t))
+            sweep.append(sweep_point(torch, mv, ctx, t, with_parity=not args.no_cpu))
             log(f"sweep context {ctx} nodes {t}: {sweep[-1]['latency_us']} us, {sweep[-1]['eff_kv_gbs']} GB/s")
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)

@@ -77,7 +77,10 @@ typedef enum {
 #define MLA_DEVERR_SLOT_RANGE 4u /* a page id < 0 or a slot >= num_kv_slots: that key is masked */
 
 /* Shapes and scalars of one call. All of it is known on the host; none of it
- * is read from device memory, so it fixes the launch shape for a capture. */
+ * is read from device memory, so it fixes the launch shape for a capture. The
+ * eight int32 fields come first and the two int64 fields after them, so the
+ * struct has no padding hole for a foreign-function mirror to get wrong
+ * (8 x 4 + 2 x 8 + 4 = 52 bytes, 56 with the tail padding). */
 typedef struct {
   int32_t batch;         /* B >= 1 requests */
   int32_t num_nodes;     /* T in [1, 64]: draft-tree nodes = verify queries per request */
@@ -95,10 +98,14 @@ typedef struct {
   float sm_scale;        /* softmax scale applied to q.k (1/sqrt(192) for 128 nope + 64 rope) */
 } mla_verify_desc;
 
-/* Bytes of workspace mla_verify_attention needs for this descriptor: a 256-byte
- * header whose first 4 bytes are the device error word, then per-split partial
- * log-sum-exps and partial outputs (fp16). Returns 0 for a descriptor that
- * mla_verify_attention would reject. */
+/* Bytes of workspace mla_verify_attention needs for this descriptor (page "The
+ * Custom sm_120 Verify Kernel ...", Part VII, "Making the Kernel CUDA Graph
+ * Capture-Safe": the split partials live in a workspace the caller allocates
+ * once, outside the captured region, so the call itself allocates nothing).
+ * Layout: a 256-byte header whose first 4 bytes are the device error word (the
+ * rest of the header is reserved), then per-split partial log-sum-exps and
+ * partial outputs (fp16). Returns 0 for a descriptor that mla_verify_attention
+ * would reject. Pure host arithmetic: no device access. */
 MLA_API size_t mla_verify_workspace_bytes(const mla_verify_desc* d);
 
 /* Ancestor bitmask of each request's draft tree (page "The Capstone Report:
@@ -133,7 +140,9 @@ MLA_API mla_status mla_build_tree_mask(const int32_t* tree_parent, uint64_t* anc
  *                the caller zeroes it when it wants to start afresh and reads
  *                it whenever it chooses. The rest is scratch.
  *   workspace_bytes: size of `workspace`; MLA_ERR_WORKSPACE if below
- *                mla_verify_workspace_bytes(d).
+ *                mla_verify_workspace_bytes(d). (An argument beyond the
+ *                problem's own list: it lets the host reject a short
+ *                workspace before anything is enqueued.)
  *   stream:      HIP stream to enqueue on (0 = the null stream).
  * Fallbacks for bad data (with the matching error bit): a bad parent makes that
  * node a root; seq_len is clamped to [T, max_pages*page_size]; a key on an
@@ -158,7 +167,8 @@ MLA_API mla_status mla_verify_partial(const mla_verify_desc* d, const void* q, c
 MLA_API mla_status mla_verify_combine(const mla_verify_desc* d, void* out, float* lse, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
-/* Static text for a status code. */
+/* Static text for a status code (the mla_status values above; no page
+ * defines them). Never null; unknown codes give "unknown status". */
 MLA_API const char* mla_status_string(mla_status s);
 
 /* MLA_VERIFY_ABI_VERSION of the built library. */

@@ -20,6 +20,10 @@ int log2i(int32_t v) {
   return r;
 }
 
+}  // namespace
+
+namespace mlav {
+
 // Shape checks shared by sizing and launching. Returns MLA_OK or the reason.
 mla_status check_desc(const mla_verify_desc* d) {
   if (d == nullptr) return MLA_ERR_NULL;
@@ -46,7 +50,9 @@ mla_status check_desc(const mla_verify_desc* d) {
   return MLA_OK;
 }
 
-}  // namespace
+}  // namespace mlav
+
+using mlav::check_desc;
 
 extern "C" {
 
@@ -66,7 +72,7 @@ mla_status mla_build_tree_mask(const int32_t* tree_parent, uint64_t* anc_mask, i
 
 }  // extern "C"
 
-namespace {
+namespace mlav {
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -121,7 +127,9 @@ mla_status prepare(const mla_verify_desc* d, const void* q, const void* kv_cache
   return MLA_OK;
 }
 
-}  // namespace
+}  // namespace mlav
+
+using mlav::prepare;
 
 extern "C" {
 

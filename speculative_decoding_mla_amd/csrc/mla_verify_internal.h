@@ -4,6 +4,8 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "mla_verify.h"
+
 namespace mlav {
 
 constexpr int kQkDim = 576;       // 512 latent + 64 rope
@@ -49,6 +51,14 @@ int col_parts_for(int batch, int nsplit, int row_blocks);
 size_t workspace_bytes(int batch, int nsplit, int rows_pad);
 size_t part_lse_offset();
 size_t part_o_offset(int batch, int nsplit, int rows_pad);
+
+// Host-side checks and the launch record (mla_verify_api.cpp); the
+// no-allocation entry point runs the same ones on its static scratch.
+mla_status check_desc(const mla_verify_desc* d);
+bool misaligned(const void* p, uintptr_t a);
+mla_status prepare(const mla_verify_desc* d, const void* q, const void* kv_cache, const int32_t* page_table,
+                   const int32_t* seq_lens, const int32_t* tree_parent, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, bool partial, bool combine, VerifyLaunch* L);
 
 hipError_t launch_tree_mask(const int32_t* tree_parent, uint64_t* anc, int batch, int nodes,
                             uint32_t* err, hipStream_t stream);

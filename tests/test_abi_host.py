@@ -43,6 +43,7 @@ def test_abi_version_and_status_strings():
     for code in range(-6, 1):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(-4) == b"workspace too small"
+    assert lib.mla_status_string(-99) == b"unknown status"
 
 
 def _desc(**kw):
@@ -214,3 +215,13 @@ def test_step_entry_points_check_arguments():
     assert lib.mla_indexer_logits(ctypes.byref(desc), a, a, a, a, a, a, None, None) == -2
     desc = bd.MlaIndexerDesc(1, 64, 128, 10, 20)
     assert lib.mla_indexer_logits(ctypes.byref(desc), a + 8, a, a, a, a, a, None, None) == -5
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py --gpus N with N > 1 exits with a message: the build runs on one GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stdout

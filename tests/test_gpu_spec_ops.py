@@ -16,7 +16,7 @@ import oracle.spec_ops_oracle as so
 import speculative_decoding_mla_amd as mv
 from oracle import bf16_bits_to_f64
 from workloads.gen import f32_to_bf16_bits
-from workloads.ops_gen import accept_case, indexer_case, sparse_case, window_case
+from workloads.ops_gen import IndexerCase, accept_case, indexer_case, sparse_case, window_case
 from tests.gpu_util import LSE_TOL, OUT_TOL, bf16, say
 
 pytestmark = pytest.mark.gpu
@@ -390,6 +390,34 @@ def test_indexer_parity(spec):
     got, err = run_indexer(c)
     assert err == 0
     check_indexer(c, got, str(spec))
+
+
+def test_indexer_widens_every_e4m3_code_exactly():
+    """gfx950's fp8 -> bf16 widening inside the indexer, over all 256 E4M3 codes
+    against torch's float8_e4m3fn decoder. Code c sits at position c of a
+    256-position request (block c // 64, row c % 64), dimension 0, all other
+    dimensions +0; head 0's query is +1 there with weight +1, head 1's is -1
+    with weight -1, every scale is 1. Every product and sum is then exact in
+    fp32 and logit = relu(d) - relu(-d) = d for each finite code d. The two NaN
+    codes are outside the workloads' domain (the generator never draws them):
+    they must not come out as finite values other than 0."""
+    codes = np.arange(256, dtype=np.uint8)
+    pos = np.arange(256, dtype=np.int64)  # (index arithmetic in uint8 would wrap)
+    blocks = np.zeros((4, 8448), np.uint8)
+    blocks[pos // 64, (pos % 64) * 128] = codes
+    blocks[:, 8192:] = np.ones((4, 64), np.float32).view(np.uint8)
+    q = np.zeros((1, 2, 128), np.uint8)
+    q[0, 0, 0], q[0, 1, 0] = 0x38, 0xB8  # +1.0, -1.0
+    c = IndexerCase(q=q, weights=np.array([[1.0, -1.0]], np.float32), blocks=blocks,
+                    block_table=np.array([[0, 1, 2, 3]], np.int32), seq_lens=np.array([256], np.int32))
+    say("indexer: all 256 e4m3 codes")
+    got, err = run_indexer(c)
+    assert err == 0
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    fin = np.isfinite(ref)
+    assert fin.sum() == 254
+    assert np.array_equal(got[0, fin], ref[fin]), np.nonzero(got[0, fin] != ref[fin])
+    assert np.all(np.isnan(got[0, ~fin]) | (got[0, ~fin] == 0))
 
 
 def test_indexer_full_table():

@@ -362,6 +362,71 @@ def test_indexer_joint_block_permutation():
     assert np.array_equal(a, b)
 
 
+def test_indexer_magnitude_bounds_every_logit():
+    """The error scale the GPU indexer check is measured against,
+    sum_h |w_h| sum_d |q_hd k_pd| s_p, must never fall below |logit|: a
+    magnitude that came out too small would tighten that check, one that came
+    out too large would loosen it. Pinned three ways: it bounds |logit| at every
+    position (the triangle inequality through the ReLU); it equals the logit
+    when every q, k and w is non-negative (no cancellation, the ReLU passes all);
+    and it equals the scalar brute force run on the absolute values (codes with
+    the sign bit cleared, |w|), which decodes each byte from its bit fields."""
+    c = indexer_case(25, batch=2, heads=6, max_blocks=3, seq_lens=[150, 64])
+    args = (c.weights, c.blocks, c.block_table, c.seq_lens)
+    lg = so.indexer_logits(c.q, *args)
+    mag = so.indexer_magnitude(c.q, *args)
+    fin = np.isfinite(lg)
+    assert np.all(mag[fin] >= np.abs(lg[fin]) * (1 - 1e-12))
+    assert np.any(mag[fin] > 2 * np.abs(lg[fin]))  # cancellation does occur in the signed case
+    assert np.all(mag[~fin] == 0)
+    # non-negative inputs: the magnitude is the logit itself
+    blocks_pos = c.blocks.copy()
+    blocks_pos[:, :8192] &= 0x7F
+    q_pos, w_pos = c.q & 0x7F, np.abs(c.weights)
+    lg_pos = so.indexer_logits(q_pos, w_pos, blocks_pos, c.block_table, c.seq_lens)
+    mag_pos = so.indexer_magnitude(q_pos, w_pos, blocks_pos, c.block_table, c.seq_lens)
+    assert np.allclose(mag_pos[fin], lg_pos[fin], rtol=1e-12, atol=0)
+    # and the scalar brute force on the absolute values
+    small = indexer_case(26, batch=1, heads=3, max_blocks=2, seq_lens=[70])
+    sb = small.blocks.copy()
+    sb[:, :8192] &= 0x7F
+    ref = np.array(so.brute_force_indexer(small.q & 0x7F, np.abs(small.weights), sb, small.block_table,
+                                          small.seq_lens))
+    got = so.indexer_magnitude(small.q, small.weights, small.blocks, small.block_table, small.seq_lens)
+    assert np.allclose(got[0, :70], ref[0, :70], rtol=1e-12, atol=0)
+
+
+def test_commit_freed_slots_hand_worked():
+    """The release list of the commit, worked by hand: the tree slots of the
+    nodes off the accepted path, in node order, then -1 (with or without
+    relocation, which moves the accepted rows and leaves their old slots to the
+    caller, who named the destinations)."""
+    # context slots 10, 11, 12; tree nodes 0..4 on slots 20..24; parents -1, 0, 0, 1, 3
+    pt = np.array([[10, 11, 12, 20, 21, 22, 23, 24, -1]], np.int32)
+    sl = np.array([8], np.int32)
+    cases = [
+        (3, [0, 1, 3], [20, 21, 23], [22, 24, -1, -1, -1]),
+        (2, [0, 2], [20, 22], [21, 23, 24, -1, -1]),
+        (1, [0], [20], [21, 22, 23, 24, -1]),
+        (4, [0, 1, 3, 4], [20, 21, 23, 24], [22, -1, -1, -1, -1]),
+    ]
+    for n_acc, chain, new_slots, freed_want in cases:
+        path = np.array([chain + [-1] * (5 - n_acc)], np.int32)
+        out_pt, ctx, freed, kv2 = so.commit_accepted(pt, sl, 5, np.array([n_acc], np.int32), path)
+        assert ctx[0] == 3 + n_acc and kv2 is None
+        assert out_pt[0, :3].tolist() == [10, 11, 12]
+        assert out_pt[0, 3:3 + n_acc].tolist() == new_slots
+        assert freed[0].tolist() == freed_want
+        kv = np.arange(60 * 576, dtype=np.uint16).reshape(60, 576)
+        dest = np.array([[40, 41, 42, 43, 44]], np.int32)
+        out_pt, _, freed_r, kv_r = so.commit_accepted(pt, sl, 5, np.array([n_acc], np.int32), path,
+                                                      dest_slots=dest, kv_bits=kv)
+        assert out_pt[0, 3:3 + n_acc].tolist() == [40 + k for k in range(n_acc)]
+        assert freed_r[0].tolist() == freed_want
+        for k, s in enumerate(new_slots):
+            assert np.array_equal(kv_r[40 + k], kv[s])
+
+
 # ================================================================== planted mistakes
 
 def _plant_decode_bias(monkeypatch):
@@ -398,6 +463,25 @@ def _plant_accept_own_target(monkeypatch):
     monkeypatch.setattr(so, "tree_accept", wrong)
 
 
+def _plant_magnitude_signed_weights(monkeypatch):
+    monkeypatch.setattr(so, "indexer_magnitude", _magnitude_signed)
+
+
+def _magnitude_signed(q_codes, weights, blocks, block_table, seq_lens):
+    # the magnitude with the weights' signs kept (|q k| summed, w signed)
+    q = np.abs(so.e4m3_to_f64(q_codes))
+    w = np.asarray(weights, dtype=np.float64)
+    out = np.zeros((q.shape[0], block_table.shape[1] * 64))
+    for b in range(q.shape[0]):
+        n = int(seq_lens[b])
+        for pg in range(-(-n // 64)):
+            codes, scales = so.indexer_block_fields(blocks[int(block_table[b, pg])])
+            mag = (np.abs(so.e4m3_to_f64(codes)) @ q[b].T) @ w[b] * np.abs(scales)
+            lo, hi = pg * 64, min(n, pg * 64 + 64)
+            out[b, lo:hi] = mag[:hi - lo]
+    return out
+
+
 def _plant_window_ceil(monkeypatch):
     monkeypatch.setattr(so, "window_start",
                         lambda length, w, p: -(-(length - min(length, w)) // p) * p)
@@ -409,6 +493,7 @@ PINS = {
     _plant_no_relu: [test_indexer_matches_torch_decode_and_matmul],
     _plant_accept_own_target: [test_accept_matches_enumeration, test_accept_hand_worked],
     _plant_window_ceil: [lambda: test_window_bound_exhaustive(4096, 64), test_window_map_holds_the_last_tokens],
+    _plant_magnitude_signed_weights: [test_indexer_magnitude_bounds_every_logit],
 }
 
 
