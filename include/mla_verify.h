@@ -68,7 +68,9 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = -3, /* head dims other than 576/512, page size not a power of two */
   MLA_ERR_WORKSPACE = -4,   /* workspace smaller than mla_verify_workspace_bytes() */
   MLA_ERR_ALIGN = -5,       /* q, kv_cache, out or workspace not 16-byte aligned */
-  MLA_ERR_HIP = -6          /* a kernel launch failed (hipGetLastError) */
+  MLA_ERR_HIP = -6,         /* a kernel launch failed (hipGetLastError) */
+  MLA_ERR_SCRATCH = -7      /* mla_verify_attention_noalloc: the problem needs more than
+                               MLA_VERIFY_NOALLOC_SCRATCH_BYTES of scratch */
 } mla_status;
 
 /* Sticky bits of the device error word (uint32). */
@@ -170,6 +172,38 @@ MLA_API mla_status mla_verify_combine(const mla_verify_desc* d, void* out, float
 /* Static text for a status code (the mla_status values above; no page
  * defines them). Never null; unknown codes give "unknown status". */
 MLA_API const char* mla_status_string(mla_status s);
+
+/* Largest scratch mla_verify_attention_noalloc can use on one GPU: calls whose
+ * mla_verify_workspace_bytes(d) exceeds it are rejected with MLA_ERR_SCRATCH. */
+#define MLA_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* mla_verify_attention for callers that cannot allocate device memory at all:
+ * code under hipGraph capture that must not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation. Instead of a caller-provided workspace, the
+ * split partials live in a static scratch array of
+ * MLA_VERIFY_NOALLOC_SCRATCH_BYTES in the library's device code: every GPU the
+ * library runs on holds one copy of it until the process ends, and its device
+ * address is looked up once per device, on the first call made with that
+ * device current (that first call is the only one that touches the HIP
+ * runtime beyond enqueuing the two kernels; it allocates nothing).
+ *   q, kv_cache, page_table, seq_lens, tree_parent, out, lse: as for
+ *                mla_verify_attention.
+ *   dev_err:     uint32 sticky device error word (MLA_DEVERR_*), caller-owned
+ *                and caller-cleared, 4-byte aligned; may be null, then data
+ *                errors still get their fallbacks but are not reported.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (concurrent streams, or
+ * threads without ordering) race and must not be made. Nothing in the scratch
+ * has to start at zero: each call writes every partial it reads back.
+ * Errors: as mla_verify_attention (no MLA_ERR_WORKSPACE), plus MLA_ERR_SCRATCH
+ * when mla_verify_workspace_bytes(d) > MLA_VERIFY_NOALLOC_SCRATCH_BYTES, and
+ * MLA_ERR_HIP when the scratch address cannot be looked up; nothing is
+ * enqueued in either case. Results are bitwise those of mla_verify_attention
+ * (the same kernels). */
+MLA_API mla_status mla_verify_attention_noalloc(const mla_verify_desc* d, const void* q, const void* kv_cache,
+                                                const int32_t* page_table, const int32_t* seq_lens,
+                                                const int32_t* tree_parent, void* out, float* lse,
+                                                uint32_t* dev_err, hipStream_t stream);
 
 /* MLA_VERIFY_ABI_VERSION of the built library. */
 MLA_API int32_t mla_verify_abi_version(void);

@@ -25,7 +25,8 @@ DEVERR_SLOT_RANGE = 4
 DEVERR_INDEX_RANGE = 8
 
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_UNSUPPORTED",
-          -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_ALIGN", -6: "MLA_ERR_HIP"}
+          -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_ALIGN", -6: "MLA_ERR_HIP", -7: "MLA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_VERIFY_NOALLOC_SCRATCH_BYTES
 
 
 class MlaVerifyDesc(ctypes.Structure):
@@ -106,6 +107,9 @@ def load_library():
         lib.mla_verify_partial.restype = ctypes.c_int
         lib.mla_verify_combine.argtypes = [ctypes.POINTER(MlaVerifyDesc), vp, vp, vp, sz, vp]
         lib.mla_verify_combine.restype = ctypes.c_int
+        lib.mla_verify_attention_noalloc.argtypes = [ctypes.POINTER(MlaVerifyDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                                     vp]
+        lib.mla_verify_attention_noalloc.restype = ctypes.c_int
         lib.mla_status_string.argtypes = [ctypes.c_int]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_verify_abi_version.argtypes = []
@@ -198,6 +202,39 @@ def verify_attention(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.
                                   _stream_handle(stream))
     if st != 0:
         raise MlaError("mla_verify_attention", st)
+
+
+def verify_attention_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, page_table: torch.Tensor,
+                             seq_lens: torch.Tensor, tree_parent: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                             dev_err: torch.Tensor | None = None, *, page_size: int, nsplit: int, sm_scale: float,
+                             stream=None) -> None:
+    """Enqueue mla_verify_attention_noalloc: the same call with no workspace (the
+    library's static per-GPU scratch holds the split partials). dev_err: an
+    optional int32 tensor whose first word receives the sticky device error bits."""
+    lib = load_library()
+    b, t, h, d = q.shape
+    _need(q.dtype == torch.bfloat16 and q.is_contiguous(), "q must be contiguous bf16 [B,T,H,576]")
+    _need(kv_cache.dtype == torch.bfloat16 and kv_cache.dim() == 2 and kv_cache.stride(1) == 1,
+          "kv_cache must be bf16 [slots, stride] with unit inner stride")
+    _need(page_table.dtype == torch.int32 and page_table.is_contiguous() and page_table.shape[0] == b,
+          "page_table must be contiguous int32 [B, max_pages]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous() and seq_lens.numel() == b,
+          "seq_lens must be int32 [B]")
+    _need(tree_parent.dtype == torch.int32 and tree_parent.is_contiguous() and tuple(tree_parent.shape) == (b, t),
+          "tree_parent must be contiguous int32 [B,T]")
+    _need(out.dtype == torch.bfloat16 and out.is_contiguous() and tuple(out.shape) == (b, t, h, HEAD_DIM_V),
+          "out must be contiguous bf16 [B,T,H,512]")
+    _need(lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (b, t, h),
+          "lse must be contiguous fp32 [B,T,H]")
+    _need(dev_err is None or (dev_err.dtype == torch.int32 and dev_err.is_cuda), "dev_err must be int32 on the GPU")
+    _need(all(x.is_cuda for x in (q, kv_cache, page_table, seq_lens, tree_parent, out, lse)),
+          "all tensors must be on the GPU")
+    desc = desc_for(q, kv_cache, page_table, page_size=page_size, nsplit=nsplit, sm_scale=sm_scale)
+    st = lib.mla_verify_attention_noalloc(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(page_table),
+                                          _ptr(seq_lens), _ptr(tree_parent), _ptr(out), _ptr(lse), _ptr(dev_err),
+                                          _stream_handle(stream))
+    if st != 0:
+        raise MlaError("mla_verify_attention_noalloc", st)
 
 
 def verify_partial(desc: MlaVerifyDesc, q, kv_cache, page_table, seq_lens, tree_parent, workspace,

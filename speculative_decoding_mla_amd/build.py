@@ -17,7 +17,8 @@ LIB_DIR = os.path.join(PKG_DIR, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmla_verify.so")
 PEAKS_PATH = os.path.join(LIB_DIR, "mla_peaks")  # measured roofline denominators
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["mla_verify_kernels.hip", "mla_verify_api.cpp", "mla_spec_ops.hip", "mla_spec_ops_api.cpp"]
+SOURCES = ["mla_verify_kernels.hip", "mla_verify_api.cpp", "mla_verify_noalloc.hip", "mla_spec_ops.hip",
+           "mla_spec_ops_api.cpp"]
 ARCH = "gfx950"
 
 # Every HIP translation unit: packed-fp32 VALU forms are kept out of the code.

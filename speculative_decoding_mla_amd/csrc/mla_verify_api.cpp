@@ -173,6 +173,7 @@ const char* mla_status_string(mla_status s) {
     case MLA_ERR_WORKSPACE: return "workspace too small";
     case MLA_ERR_ALIGN: return "misaligned pointer";
     case MLA_ERR_HIP: return "kernel launch failed";
+    case MLA_ERR_SCRATCH: return "problem needs more than the no-allocation scratch (MLA_VERIFY_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

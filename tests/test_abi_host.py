@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"mla_verify_workspace_bytes", "mla_build_tree_mask", "mla_verify_attention",
                           "mla_verify_partial", "mla_verify_combine", "mla_status_string",
-                          "mla_verify_abi_version"}
+                          "mla_verify_abi_version", "mla_verify_attention_noalloc"}
     ops = declared_functions(HEADER_OPS)
     assert set(ops) == {"mla_sparse_decode_workspace_bytes", "mla_sparse_decode", "mla_kv_append",
                         "mla_tree_accept", "mla_commit_accepted", "mla_accept_commit", "mla_window_map",
@@ -40,9 +40,10 @@ def test_exports_every_declared_symbol():
 def test_abi_version_and_status_strings():
     lib = bd.load_library()
     assert lib.mla_verify_abi_version() == 1
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert lib.mla_status_string(code)
     assert lib.mla_status_string(-4) == b"workspace too small"
+    assert b"scratch" in lib.mla_status_string(-7)
     assert lib.mla_status_string(-99) == b"unknown status"
 
 
@@ -225,3 +226,22 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stdout
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """The no-allocation entry point checks the descriptor and its size against
+    the static scratch (64 MiB) on the host, before any HIP call: these return
+    without a GPU."""
+    lib = bd.load_library()
+    cap = 64 << 20
+    big = _desc(batch=8, num_nodes=64, num_heads=8, nsplit=256)  # 8 x 256 x 512 rows x 1 KiB: far past the cap
+    assert bd.workspace_bytes(big) > cap
+    dummy = ctypes.c_void_p(16)
+    args = [dummy] * 7
+    assert lib.mla_verify_attention_noalloc(ctypes.byref(big), *args, None, None) == -7
+    bad = _desc(num_nodes=0)
+    assert lib.mla_verify_attention_noalloc(ctypes.byref(bad), *args, None, None) == -2
+    ok = _desc(batch=1, num_nodes=9, nsplit=256)
+    assert bd.workspace_bytes(ok) <= cap
+    # misaligned error word: rejected before the scratch lookup
+    assert lib.mla_verify_attention_noalloc(ctypes.byref(ok), *args, ctypes.c_void_p(18), None) == -5
