@@ -82,13 +82,19 @@ constexpr int kTileBytes = kKeysPerTile * kRowBytes;               // 36864
 constexpr int kRopeInstr = kKeysPerTile * kRopeBytes / 1024;       // 4 loads of 8 keys' rope
 constexpr int kTileInstr = kKeysPerTile + kRopeInstr;              // 36 wave-wide 1 KiB loads
 constexpr int kStages = 4;
-constexpr int kSlotCap = 2048;
+constexpr int kWaves = 4;  // per partial workgroup: one per SIMD
 constexpr int kQSteps = kQkDim / 16;                               // 36 k-steps of 16
 constexpr int kColBlocks = kVDim / 32;                             // 16
 constexpr float kRefLift = 32.0f;  // log2 units: reference above the max of the split's first tile
 constexpr float kRefHead = 96.0f;  // log2 units: largest weight kept is 2^kRefHead
 constexpr float kHeadWeight = 0x1p96f;  // 2^kRefHead
 static_assert(kRefHead == 96.0f, "kHeadWeight must stay 2^kRefHead");
+
+// Source of the keys that no row may see (an out-of-range or unused slot, the
+// padding past a request's last key): a row of zeros, so that such keys enter
+// both products as exact zeros whatever the pool holds (a weight of 0 times a
+// non-finite value is not 0). Never written.
+__device__ __align__(256) uint8_t kZeroRow[kRowBytes];
 
 // 16-byte chunk permutation inside a 128-byte group, keyed by the key's index
 // in the tile: 8 consecutive keys hit 8 distinct slots (K reads), and the
@@ -321,28 +327,38 @@ constexpr int kPassFixed = 2;     // accumulate against a given reference
 // kSparse: one query token per request over an index list (sparse top-k
 // decode): lengths may be absent, an entry of -1 is unused, every node is a
 // root. A compile-time switch, so the verify instantiations carry none of it.
+// NWQ: waves that own query rows (32 each). Every workgroup runs kWaves waves:
+// all of them stream key tiles (wave w loads keys 8w..8w+7 of each tile), the
+// first NWQ also compute.
 // NCP: column parts. With NCP > 1, NCP workgroups share a (split, row block):
 // each computes the same scores and weights but only its 512/NCP output
 // columns (kCB column blocks), so a grid that would leave CUs idle spreads the
 // PV products, the normalisation and the partial stores over NCP CUs.
-template <int NW, bool kSparse, int NCP>
-__global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch L) {
+//
+// Split s of a request that owns nsb split slots takes the request's key tiles
+// s, s + nsb, s + 2 nsb, ... (tile g = keys 32g .. 32g + 31). The keys of a
+// split are a subset like any other for the merge; taken this way, the first
+// tiles of a split do not depend on the request's length, so for one request
+// their page-table entries are requested together with the length.
+template <int NWQ, bool kSparse, int NCP>
+__global__ __launch_bounds__(kWaves * 64, 1) void verify_partial_kernel(VerifyLaunch L) {
   constexpr int kCB = kColBlocks / NCP;
-  constexpr int kInstrPerWave = kTileInstr / NW;
-  static_assert(kTileInstr % NW == 0, "tile loads must split evenly over the waves");
-  constexpr int kTilesPerWindow = kSlotCap / kKeysPerTile;
+  constexpr int kLoadsPerTile = kTileInstr / kWaves;  // 8 latent rows + the rope parts of those 8 keys
+  constexpr int kLoadsPerStep = kLoadsPerTile + 1;    // + the page-table entries of a later tile
+  static_assert(kLoadsPerTile == 9 && kKeysPerTile == 8 * kWaves, "a wave streams 8 keys of every tile");
+  constexpr int kPeRing = 4;   // page-table entries of tiles k .. k+3 (one slot per lane and wave)
+  constexpr int kBadRing = 8;  // bad-key bits of recent tiles
 
   __shared__ __attribute__((aligned(1024))) uint8_t kv_s[kStages * kTileBytes];
-  __shared__ int32_t slot_s[kSlotCap];
-  __shared__ int32_t pt_s[kSlotCap / 2 + 1];  // page-table entries of a window of pages of 2+ keys
-  __shared__ uint32_t badbits_s[kTilesPerWindow];  // bit k: key k of the tile sits on a bad slot
+  __shared__ int32_t pe_s[kPeRing][kWaves][64];
+  __shared__ uint32_t bad_s[kBadRing];  // byte w of entry k % kBadRing: keys 8w..8w+7 of tile k on a bad slot
   __shared__ uint64_t anc_s[kMaxNodes];
-  __shared__ int32_t badw_s[NW];
-  __shared__ int32_t over_s[NW];
+  __shared__ int32_t over_s[kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int hsel = lane >> 5;
+  const bool qk_wave = wid < NWQ;
 
   // XCD-aware order: workgroup i runs on XCD i % 8, so consecutive logical ids
   // (the column parts and row blocks of one split) are placed on one XCD in
@@ -359,66 +375,52 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   if (sr.b < 0) return;  // idle slot: no request owns it and the combine never reads it
   const int b = __builtin_amdgcn_readfirstlane(sr.b);
   const int s = slot - __builtin_amdgcn_readfirstlane(sr.first);
-  const int nsplit_b = __builtin_amdgcn_readfirstlane(sr.count);
+  const int nsb = __builtin_amdgcn_readfirstlane(sr.count);
 
   const int T = L.nodes;
-  const int row = rb * (NW * 32) + wid * 32 + (lane & 31);
-  const bool row_ok = row < L.rows;
-
-  // The chain before the first key tile is length -> page table -> keys;
-  // the tree parents (wave 0) are requested with the length, the query rows
-  // (below) right after the page-table entries, so that their loads do not
-  // hold up the length.
-  const int n_raw = kSparse ? raw_len(L, b) : L.seq_lens[b];
-  int parent = -1;
-  if (!kSparse && wid == 0 && lane < T) parent = L.tree_parent[static_cast<size_t>(b) * T + lane];
+  const int row = rb * (NWQ * 32) + wid * 32 + (lane & 31);
+  const bool row_ok = qk_wave && row < L.rows;
 
   const uint32_t lds_kv = lds_addr(kv_s);
   const uint32_t lane16 = lane * 16;
-  const uint32_t row_bytes32 = static_cast<uint32_t>(L.kv_row_bytes);  // < 2^31 (checked on the host)
+  const uint64_t row_bytes = static_cast<uint64_t>(L.kv_row_bytes);
 
-  const int n = min(max(n_raw, kSparse ? 0 : T), L.capacity);
-  if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
-  const int ctx = n - T;
-  const int chunk = (n + nsplit_b - 1) / nsplit_b;
-  const int k0 = s * chunk;
-  const int k1 = min(n, k0 + chunk);
-
-  f32x2* lse_dst =
-      reinterpret_cast<f32x2*>(L.part_lse) + (static_cast<size_t>(slot) * kMaxColParts + cp) * L.rows_pad + row;
-  if (k0 >= k1) {  // empty split: contributes nothing
-    if (lane < 32) store_agent8(lse_dst, f32x2{-INFINITY, 0.f});
-    return;
-  }
-
-  // Page-table entries of the keys [w0, w0 + wn), one wave-wide 4-byte
-  // global->LDS load per 64 entries: with one key per page straight into
-  // slot_s (each entry is then checked in place by the thread that owns its
-  // key), with larger pages into pt_s; the window's bad-key bits are cleared
-  // beside them. Pages pg0.. of the window lie below max_pages.
-  auto request_window = [&](int w0, int wn) {
-    const int pg0 = w0 >> L.page_shift;
-    const int npg = ((w0 + wn - 1) >> L.page_shift) - pg0 + 1;
-    const int32_t* pt = L.page_table + static_cast<size_t>(b) * L.max_pages + pg0;
-    const uint32_t pt_lds = lds_addr(L.page_shift == 0 ? slot_s : pt_s);
-    const int ln = fresh(lane);
-    for (int j0 = wid * 64; j0 < npg; j0 += NW * 64)
-      if (j0 + ln < npg) dma4(pt + j0 + ln, pt_lds + j0 * 4);
-    const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
-    for (int i = fresh(static_cast<int>(threadIdx.x)); i < ntiles; i += NW * 64) badbits_s[i] = 0u;
+  // This lane's key in every tile: the wave streams keys 8 wid .. 8 wid + 7
+  // (a 1 KiB latent load per key, one load for the rope parts of all eight),
+  // and lane l's key, page-table entry and rope chunks are key 8 wid + l / 8.
+  const int lkey = 8 * wid + (lane >> 3);
+  const int32_t* pt_row = L.page_table + static_cast<size_t>(b) * L.max_pages;
+  const uint32_t lds_pe = lds_addr(&pe_s[0][wid][0]);
+  // Page-table entry of this lane's key in local tile k of the split (global
+  // tile s + k nsb), into ring slot k % kPeRing. Positions past the table
+  // read its last entry (such a key lies past the length and is never used).
+  auto issue_pe = [&](int k) {
+    // (64-bit: k runs up to five tiles past the split's last one)
+    const int64_t p = (static_cast<int64_t>(s) + static_cast<int64_t>(k) * nsb) * kKeysPerTile + lkey;
+    const int pc = static_cast<int>(min(p, static_cast<int64_t>(L.capacity - 1)));
+    dma4(pt_row + (pc >> L.page_shift), lds_pe + (k % kPeRing) * (kWaves * 256));
   };
-  request_window(k0, min(k1 - k0, kSlotCap));
 
-  // This wave's 32 query rows go to KV stage `wid` in the layout of a key
-  // tile (row k of the wave in the place of key k), with the same
+  // The length (scalar load) and the tree parents (wave 0); the page-table
+  // entries of the split's first three tiles, which do not depend on the
+  // length; then the query rows of the computing waves. For one request
+  // nothing here waits for anything else.
+  const int n_raw = kSparse ? raw_len(L, b) : L.seq_lens[b];
+  int parent = -1;
+  if (!kSparse && wid == 0 && lane < T) parent = L.tree_parent[static_cast<size_t>(b) * T + lane];
+  issue_pe(0);
+  issue_pe(1);
+  issue_pe(2);
+  // A computing wave's 32 query rows go to KV stage `wid` in the layout of a
+  // key tile (row k of the wave in the place of key k), with the same
   // line-coalesced global->LDS loads; each lane then reads its B operands of
   // S^T = K Q^T from there exactly as it reads K fragments. (Loaded straight
   // into registers, every load instruction would gather 32 bytes from each
   // of 32 rows, and the rows of four waves do not fit the L1: each line came
   // from L2 four times over.) Padding rows load row 0 of the request; their
   // results are never stored.
-  {
-    const int r0 = rb * (NW * 32) + wid * 32;  // wave-uniform
+  if (qk_wave) {
+    const int r0 = rb * (NWQ * 32) + wid * 32;  // wave-uniform
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(L.q) + static_cast<size_t>(b) * L.rows * kRowBytes;
     const uint32_t stage = lds_kv + wid * kTileBytes;
 #pragma unroll 4
@@ -434,9 +436,30 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
             stage + kRopeBase + g * 1024);
     }
   }
+  wait_vmcnt<0>();
+
+  const int n = min(max(n_raw, kSparse ? 0 : T), L.capacity);
+  if (n != n_raw && threadIdx.x == 0 && s == 0 && rb == 0 && cp == 0) atomicOr(L.err, MLA_DEVERR_SEQ_LEN);
+  const int ctx = n - T;
+  const int ntot = (n + kKeysPerTile - 1) / kKeysPerTile;  // key tiles of the request
+  const int ntiles = s < ntot ? (ntot - 1 - s) / nsb + 1 : 0;
+
+  f32x2* lse_dst =
+      reinterpret_cast<f32x2*>(L.part_lse) + (static_cast<size_t>(slot) * kMaxColParts + cp) * L.rows_pad + row;
+  if (ntiles == 0) {  // empty split: contributes nothing (every load above has landed)
+    if (qk_wave && lane < 32) store_agent8(lse_dst, f32x2{-INFINITY, 0.f});
+    return;
+  }
+
+  // Ancestor-or-self masks of the request's nodes (wave 0), read by every
+  // row's lane after the barrier; sparse decode: every node is a root.
+  if (wid == 0) {
+    const int ln = fresh(lane);
+    anc_s[ln] = kSparse ? (ln < T ? 1ull << ln : 0ull) : ancestor_bits_of(parent, T, ln, L.err);
+  }
+  lds_barrier();
 
   bf16x8 qf[kQSteps];  // lane: dims 16ks + 8*hsel + 0..7 of row lane%32
-  const bool need_mask = k1 > ctx;
   uint64_t my_anc = 0;
 
   // Per-lane LDS offsets that do not change from tile to tile.
@@ -467,6 +490,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     if (ks < kVDim / 16) return *reinterpret_cast<const bf16x8*>(st + koff[ks & 3] + (ks >> 2) * 128);
     return *reinterpret_cast<const bf16x8*>(st + koff[ks & 3] + krope);
   };
+
   // One MFMA step of S^T = K Q^T. The accumulator lives in VGPRs (the AGPR
   // file holds the whole O^T accumulator), so the step is issued as inline
   // asm with a VGPR destination: back-to-back accumulation into the same
@@ -493,15 +517,60 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
     return acc;
   };
 
+  // Row address of this lane's key in local tile k, from its page-table entry
+  // in the ring: keys past the length, on an out-of-range slot or on an unused
+  // (-1) index entry read the zero row instead, so that they enter both
+  // products as exact zeros. Records the tile's bad-key bits (keys inside the
+  // length that cannot be loaded) for the mask, and flags the bad ones.
+  auto tile_addr = [&](int k) -> uint64_t {
+    const int p = (s + k * nsb) * kKeysPerTile + lkey;
+    const int32_t page = pe_s[k % kPeRing][wid][lane];
+    const int64_t slot_id = (static_cast<int64_t>(page) << L.page_shift) + (p & ((1 << L.page_shift) - 1));
+    const bool in_len = p < n;
+    const bool ok = in_len && page >= 0 && slot_id < L.num_slots;
+    const uint64_t addr = ok ? reinterpret_cast<uint64_t>(L.kv) + static_cast<uint64_t>(slot_id) * row_bytes
+                             : reinterpret_cast<uint64_t>(kZeroRow);
+    const uint64_t badm = __ballot(in_len && !ok);
+    uint32_t byte = 0;
+    if (badm != 0) {  // rare: one bit per key (lanes 8j hold key 8 wid + j)
+      const uint64_t errm = kSparse ? __ballot(in_len && !ok && page != -1) : badm;
+      if (errm != 0 && lane == 0) atomicOr(L.err, MLA_DEVERR_SLOT_RANGE);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) byte |= static_cast<uint32_t>((badm >> (8 * j)) & 1u) << j;
+    }
+    if (lane == 0) reinterpret_cast<uint8_t*>(bad_s)[(k % kBadRing) * kWaves + wid] = static_cast<uint8_t>(byte);
+    return addr;
+  };
+  // Load i of this wave for a tile whose key addresses are `addr`: the 1 KiB
+  // latent part of key 8 wid + i (i < 8; its row address is wave-uniform), or
+  // the rope parts of all eight keys (i = 8; a row address per lane).
+  auto issue_one = [&](int k, int i, uint64_t addr) {
+    const uint32_t stage = lds_kv + (k % kStages) * kTileBytes;
+    if (i < 8) {
+      const int key = 8 * wid + i;
+      const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(addr), 8 * i);
+      const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(addr >> 32), 8 * i);
+      const void* rowp = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+      dma16_row(rowp, lane16, swz(key) << 4, stage, key * kLatentBytes);
+    } else {
+      const uint32_t chunk = (kVDim / 8 + ((lane & 7) ^ swz(lkey))) << 4;
+      dma16(reinterpret_cast<const uint8_t*>(addr) + chunk, stage + kRopeBase + wid * 1024);
+    }
+  };
+  auto issue_tile = [&](int k, uint64_t addr) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) issue_one(k, i, addr);
+  };
+
   // Visibility of the tile's 32 keys for this lane's row: context keys are
   // visible to every node, a tree key C + j only to the nodes with j in their
-  // ancestor set, keys past the window or on a bad slot to nobody.
-  auto visible_bits = [&](int w0, int wn, int t) -> uint32_t {
-    const int tk0 = t * kKeysPerTile;
-    const int a = w0 + tk0 - ctx;  // key k of the tile is tree node a + k when a + k >= 0
-    const int left = wn - tk0;
+  // ancestor set, keys past the length or on a bad slot to nobody.
+  auto visible_bits = [&](int k) -> uint32_t {
+    const int p0 = (s + k * nsb) * kKeysPerTile;
+    const int a = p0 - ctx;  // key k of the tile is tree node a + k when a + k >= 0
+    const int left = n - p0;
     uint32_t bits = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
-    bits &= ~badbits_s[t];
+    bits &= ~bad_s[k % kBadRing];
     // Keys before the tree (a + k < 0) are visible; node j = a + k is visible
     // when bit j of the ancestor mask is set. Selects, not branches: the
     // shifts are clamped to [0, 63] and the out-of-range cases chosen after.
@@ -616,13 +685,19 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
   };
   auto nothing = [](int) {};
 
-  // One pass over the split's keys: windows of up to kSlotCap keys; tiles of
-  // 32 keys streamed through kStages LDS buffers. Iteration t overlaps the
-  // scores of tile t+1 (MFMA) with the softmax of tile t (VALU), then the PV
-  // product of tile t (MFMA) with the masking of tile t+1's scores (VALU).
-  auto run_pass = [&](auto mode_tag) {
+  // One pass over the split's tiles, streamed through kStages LDS buffers.
+  // Step t overlaps the scores of tile t+1 (MFMA) with the softmax of tile t
+  // (VALU), then the PV product of tile t (MFMA) with the masking of tile
+  // t+1's scores (VALU); every wave issues its loads of tile t+3 in between
+  // and requests the page-table entries of tile t+5.
+  // kCompute: the wave owns query rows. A wave without rows runs the same
+  // pass with the same waits and barriers but only streams its keys: the two
+  // kinds of wave never share a code path while the accumulator is live, so
+  // it stays in the AGPRs.
+  auto run_pass = [&](auto mode_tag, auto compute_tag) {
     constexpr int kMode = decltype(mode_tag)::value;
-    constexpr bool kAccum = kMode != kPassMaxOnly;
+    constexpr bool kCompute = decltype(compute_tag)::value;
+    constexpr bool kAccum = kMode != kPassMaxOnly && kCompute;
     if constexpr (kAccum) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) o[cb] = f32x16{};
@@ -630,247 +705,182 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_partial_kernel(VerifyLaunch
       l_pb = 0.f;
     }
     mu = kMode == kPassFixed && m_ref != -INFINITY ? m_ref : 0.f;
-    for (int w0 = k0; w0 < k1; w0 += kSlotCap) {
-      const int wn = min(k1 - w0, kSlotCap);
-      const int ntiles = (wn + kKeysPerTile - 1) / kKeysPerTile;
-      // The first window of the first pass was requested in the prologue,
-      // together with the query rows; any other is requested once everyone
-      // is done with the previous window or pass.
-      const bool first = kMode == kPassAdaptive && w0 == k0;
-      if (!first) {
-        lds_barrier();
-        request_window(w0, wn);
-      }
+    // The first pass's first page-table entries were requested in the
+    // prologue; another pass requests them again once every wave is done with
+    // the stages of the previous one.
+    if constexpr (kMode != kPassAdaptive) {
+      lds_barrier();
+      issue_pe(0);
+      issue_pe(1);
+      issue_pe(2);
       wait_vmcnt<0>();
-      lds_barrier();
-      if (first) {  // the wave's query rows, from its own stage, into registers
-#pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = ld_k(kv_s + wid * kTileBytes, ks);
-      }
-      const int pg0 = w0 >> L.page_shift;
-      const int32_t* ptab = L.page_shift == 0 ? slot_s : pt_s;
-      // Physical slot of every key in this window; bad slots are recorded in
-      // the tile's bad-key bits and loaded from slot 0 instead.
-      int bad = 0;
-      for (int i = fresh(static_cast<int>(threadIdx.x)); i < wn; i += NW * 64) {
-        const int p = w0 + i;
-        const int page = ptab[(p >> L.page_shift) - pg0];
-        const int64_t slot = (static_cast<int64_t>(page) << L.page_shift) + (p & ((1 << L.page_shift) - 1));
-        const bool ok = page >= 0 && slot < L.num_slots;
-        slot_s[i] = ok ? static_cast<int32_t>(slot) : 0;
-        if (!ok) {
-          atomicOr(&badbits_s[i >> 5], 1u << (i & 31));
-          // an unused entry (-1) of a sparse index list is masked quietly
-          if (!(kSparse && page == -1)) bad = 1;
-        }
-      }
-      const int wave_bad = __any(bad);
-      if (lane == 0) badw_s[wid] = wave_bad;
-      if (kMode == kPassAdaptive && need_mask && w0 == k0 && wid == 0) {
-        // sparse decode: every node is a root (one query token per request)
-        const int ln = fresh(lane);
-        const uint64_t a = kSparse ? (ln < T ? 1ull << ln : 0ull) : ancestor_bits_of(parent, T, ln, L.err);
-        anc_s[ln] = a;
-      }
-      lds_barrier();
-      if (kMode == kPassAdaptive) {
-        bool win_bad = false;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) win_bad |= badw_s[w] != 0;
-        if (win_bad && threadIdx.x == 0) atomicOr(L.err, MLA_DEVERR_SLOT_RANGE);
-        if (need_mask && w0 == k0) {
-          const int r = rb * (NW * 32) + wid * 32 + (fresh(lane) & 31);
-          my_anc = anc_s[(r < L.rows ? r : 0) / fresh(L.heads)];  // this lane's node (divisor rebuilt here too)
-        }
-      }
+    }
+    // Tiles 0-2, with the entries of tiles 3 and 4 requested between them in
+    // the order the steps keep: entries of tile k + 2, then the loads of k.
+    issue_tile(0, tile_addr(0));
+    if (ntiles > 1) {
+      issue_pe(3);
+      issue_tile(1, tile_addr(1));
+    }
+    if (ntiles > 2) {
+      issue_pe(4);
+      issue_tile(2, tile_addr(2));
+    }
 
-      // Slots behind this wave's loads of tile t: load i is the latent part of
-      // key wid + i*NW (one wave-uniform slot) or, for i*NW + wid >= 32, the
-      // rope parts of eight keys (a slot per lane).
-      // Load i of this wave for a tile: the latent part of one key (a 1 KiB
-      // row, one slot for the whole wave) or the rope parts of eight keys.
-      // The assignment makes every load of NW = 1, 2, 4 and all but load 10
-      // of NW = 3 the same kind on every wave, so that, with i known after
-      // unrolling, the kind is a compile-time constant.
-      auto ins_of = [&](int i) -> int {
-        if constexpr (NW == 3)
-          return i < 10 ? wid + 3 * i : (i == 10 ? (wid < 2 ? 30 + wid : kKeysPerTile + 3) : kKeysPerTile + wid);
-        else
-          return wid + i * NW;
-      };
-      auto slot_of = [&](int t, int i) -> int32_t {
-        const int ins = ins_of(i);
-        const int key = ins < kKeysPerTile ? ins : 8 * (ins - kKeysPerTile) + (lane >> 3);
-        return slot_s[min(t * kKeysPerTile + key, wn - 1)];  // keys past the window reload a real row
-      };
-      auto issue_one = [&](int t, int i, int32_t slot) {
-        const int ins = ins_of(i);  // wave-uniform
-        const uint32_t stage = lds_kv + (t % kStages) * kTileBytes;
-        const bool all_latent = NW == 3 ? i < 10 : i < kKeysPerTile / NW;
-        if (all_latent) {  // row address in SGPRs, lane offset in a VGPR
-          const uint32_t s32 = __builtin_amdgcn_readfirstlane(slot);  // >= 0
-          dma16_row(L.kv + static_cast<uint64_t>(s32) * row_bytes32, lane16, swz(ins) << 4, stage,
-                    ins * kLatentBytes);
-        } else {  // rope parts, or (NW = 3, load 10) either kind: selects, not branches
-          const bool latent = ins < kKeysPerTile;
-          const int g = ins - kKeysPerTile;
-          const int rkey = 8 * g + (lane >> 3);
-          const uint32_t chunk =
-              latent ? (lane16 ^ (swz(ins) << 4)) : ((kVDim / 8 + ((lane & 7) ^ swz(rkey))) << 4);
-          const uint32_t dst = stage + (latent ? ins * kLatentBytes : kRopeBase + g * 1024);
-          dma16(L.kv + static_cast<uint64_t>(static_cast<uint32_t>(slot)) * row_bytes32 + chunk, dst);
-        }
-      };
-      auto issue_tile = [&](int t) {
-#pragma unroll 3
-        for (int i = 0; i < kInstrPerWave; ++i) issue_one(t, i, slot_of(t, i));
-      };
+    // Scores of tile 0 (loads complete in issue order: tiles 1 and 2 may
+    // still be in flight).
+    if (ntiles >= 3) wait_vmcnt<2 * kLoadsPerStep>();
+    else if (ntiles == 2) wait_vmcnt<kLoadsPerStep>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    float tsc[16];
+    if constexpr (kCompute) scale_mask(qk(kv_s), visible_bits(0), tsc);
+    if constexpr (kCompute && kMode == kPassAdaptive) {
+      // The split's first tile fixes each row's reference: its max +
+      // kRefLift (room for scores up to kRefLift + kRefHead above it). A row
+      // it shows no key to keeps none; should a later tile show it one, the
+      // split takes the exact path.
+      float mx = tsc[0];
 #pragma unroll
-      for (int t = 0; t < kStages - 1; ++t)
-        if (t < ntiles) issue_tile(t);
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, tsc[j]);
+      mx = fmaxf(mx, xor32(mx));
+      m_ref = mx + kRefLift;  // -inf stays -inf
+      mu = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) tsc[j] -= mu;  // these scores were taken unshifted
+      unset = m_ref == -INFINITY;
+    }
 
-      // Scores of tile 0 (loads complete in issue order: tiles 1 and 2 may
-      // still be in flight).
-      if (ntiles >= 3) wait_vmcnt<2 * kInstrPerWave>();
-      else if (ntiles == 2) wait_vmcnt<kInstrPerWave>();
+    // Step t: scores of tile t+1, softmax and PV of tile t, loads of tile
+    // t+3. The steps that issue loads and the last two (which issue none)
+    // are separate loops, so the steady state has no branches.
+    auto step = [&](auto dma_tag, int t) {
+      constexpr bool dma_next = decltype(dma_tag)::value;
+      // Tile t+1 has landed (this wave's part, and with it the page-table
+      // entries of tile t+3) once only the loads of the last step are
+      // outstanding; the barrier also retires PV(t-1), freeing the stage that
+      // tile t+3 loads into.
+      if (dma_next || t + 2 < ntiles) wait_vmcnt<kLoadsPerStep>();
       else wait_vmcnt<0>();
       lds_barrier();
-      float tsc[16];
-      const bool sees = scale_mask(qk(kv_s), visible_bits(w0, wn, 0), tsc);
-      if constexpr (kMode == kPassAdaptive) {
-        if (w0 == k0) {
-          // The split's first tile fixes each row's reference: its max +
-          // kRefLift (room for scores up to kRefLift + kRefHead above it).
-          // A row it shows no key to keeps none; should a later tile show
-          // it one, the split takes the exact path.
-          float mx = tsc[0];
-#pragma unroll
-          for (int j = 1; j < 16; ++j) mx = fmaxf(mx, tsc[j]);
-          mx = fmaxf(mx, xor32(mx));
-          m_ref = mx + kRefLift;  // -inf stays -inf
-          mu = m_ref == -INFINITY ? 0.f : m_ref;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) tsc[j] -= mu;  // these scores were taken unshifted
-          unset = m_ref == -INFINITY;
-        } else {
-          overflow |= unset && sees;
-        }
+      uint64_t a3 = 0;
+      if constexpr (dma_next) {
+        a3 = tile_addr(t + 3);
+        issue_pe(t + 5);
       }
+      if constexpr (!kCompute) {  // a wave without query rows only streams its keys
+        if constexpr (dma_next) issue_tile(t + 3, a3);
+        return;
+      }
+      const uint8_t* st = kv_s + (t % kStages) * kTileBytes;
+      const uint8_t* st1 = kv_s + ((t + 1) % kStages) * kTileBytes;
 
-      // Step t: scores of tile t+1, softmax and PV of tile t, loads of tile
-      // t+3. The steps that issue loads and the last two (which issue none)
-      // are separate loops, so the steady state has no branches.
-      auto step = [&](auto dma_tag, int t) {
-        constexpr bool dma_next = decltype(dma_tag)::value;
-        // Tile t+1 has landed (this wave's part) once only tiles issued after
-        // it are outstanding; the barrier also retires PV(t-1), freeing the
-        // stage that tile t+3 loads into.
-        if (dma_next || t + 2 < ntiles) wait_vmcnt<kInstrPerWave>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        const uint8_t* st = kv_s + (t % kStages) * kTileBytes;
-        const uint8_t* st1 = kv_s + ((t + 1) % kStages) * kTileBytes;
-
-        // phase 1: the 36 MFMAs of QK(t+1) with K fragments prefetched four
-        // steps ahead; between them the softmax of tile t (VALU) and the loads
-        // of tile t+3, spread over the chain (load i after step i*E + E-1,
-        // its slot read from LDS three steps earlier).
-        bf16x8 pf[2];
-        {
-          f32x16 acc;
-          bf16x8 kf[4];
-          SoftmaxState sm;
-          constexpr int kDmaEvery = kQSteps / kInstrPerWave;
-          constexpr int kSlotLead = 3;
-          int32_t slr[4];
-#pragma unroll
-          for (int i = 0; i < kInstrPerWave && i * kDmaEvery + kDmaEvery - 1 < kSlotLead; ++i)
-            if constexpr (dma_next) slr[i & 3] = slot_of(t + 3, i);
-#pragma unroll
-          for (int p = 0; p < 4; ++p) kf[p] = ld_k(st1, p);
-          static_for<kQSteps>([&](auto ks_c) {
-            constexpr int ks = decltype(ks_c)::value;
-            qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
-            if constexpr (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st1, ks + 4);
-            if constexpr (ks % 2 == 0 && ks / 2 < (kMode == kPassMaxOnly ? 10 : 9)) {
-              softmax_piece(mode_tag, ks / 2, sm, tsc, pf);
-              anchor(mode_tag, ks / 2, sm, pf);
-            }
-            if constexpr (dma_next) {
-              constexpr int ahead = ks + kSlotLead;  // step whose load needs its slot now
-              if constexpr (ahead < kQSteps && ahead % kDmaEvery == kDmaEvery - 1)
-                slr[(ahead / kDmaEvery) & 3] = slot_of(t + 3, ahead / kDmaEvery);
-              if constexpr (ks % kDmaEvery == kDmaEvery - 1)
-                issue_one(t + 3, ks / kDmaEvery, slr[(ks / kDmaEvery) & 3]);
-            }
-          });
-          qk_done(acc);
-
-          // phase 2: PV(t) on the matrix cores; the masking of tile t+1's
-          // scores (one element per step) on the VALU in between.
-          const uint32_t vsh = visible_bits(w0, wn, t + 1) >> (4 * hsel);
-          // (16 elements over 2*kCB steps: one per step, or 16/(2*kCB))
-          constexpr int kMaskPer = 2 * kCB >= 16 ? 1 : 16 / (2 * kCB);
-          // Scale on the VALU between the MFMAs; the mask after them, and only
-          // for a tile that is not wholly visible (tree keys, the end of the
-          // window, bad slots): a tile of context keys needs none.
-          auto scale_step = [&](int i) {
-#pragma unroll
-            for (int k = 0; k < kMaskPer; ++k) {
-              const int m = i * kMaskPer + k;
-              if (m < 16) {
-                tsc[m] = fmaf(acc[m], L.scale_log2, -mu);
-                asm volatile("" : "+v"(tsc[m]));
-              }
-            }
-          };
-          if constexpr (kAccum) {
-            pv(st, pf, scale_step);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) scale_step(i);
-          }
-          const int tk1 = (t + 1) * kKeysPerTile;
-          const bool all_visible = w0 + tk1 + kKeysPerTile <= ctx && wn - tk1 >= kKeysPerTile &&
-                                   __builtin_amdgcn_readfirstlane(badbits_s[t + 1]) == 0u;
-          if (!all_visible) {
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              tsc[m] = ((vsh >> (8 * (m >> 2) + (m & 3))) & 1u) ? tsc[m] : -INFINITY;
-              asm volatile("" : "+v"(tsc[m]));  // (keeps the branch: no speculative selects)
-            }
-            if constexpr (kMode == kPassAdaptive) overflow |= unset && (vsh & 0x0f0f0f0fu) != 0u;
-          } else {
-            if constexpr (kMode == kPassAdaptive) overflow |= unset;
-          }
-        }
-      };
-      int t = 0;
-      for (; t + 3 < ntiles; ++t) step(BoolTag<true>{}, t);
-      for (; t + 1 < ntiles; ++t) step(BoolTag<false>{}, t);
-      // last tile of the window
+      // phase 1: the 36 MFMAs of QK(t+1) with K fragments prefetched four
+      // steps ahead; between them the softmax of tile t (VALU) and the loads
+      // of tile t+3 (one after every fourth MFMA).
+      bf16x8 pf[2];
       {
-        bf16x8 pf[2];
-        softmax(mode_tag, tsc, pf);
-        if constexpr (kAccum) pv(kv_s + ((ntiles - 1) % kStages) * kTileBytes, pf, nothing);
+        f32x16 acc;
+        bf16x8 kf[4];
+        SoftmaxState sm;
+        constexpr int kDmaEvery = kQSteps / kLoadsPerTile;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) kf[p] = ld_k(st1, p);
+        static_for<kQSteps>([&](auto ks_c) {
+          constexpr int ks = decltype(ks_c)::value;
+          qk_step(acc, kf[ks & 3], qf[ks], ks == 0);
+          if constexpr (ks + 4 < kQSteps) kf[ks & 3] = ld_k(st1, ks + 4);
+          if constexpr (ks % 2 == 0 && ks / 2 < (kMode == kPassMaxOnly ? 10 : 9)) {
+            softmax_piece(mode_tag, ks / 2, sm, tsc, pf);
+            anchor(mode_tag, ks / 2, sm, pf);
+          }
+          if constexpr (dma_next && ks % kDmaEvery == kDmaEvery - 1) issue_one(t + 3, ks / kDmaEvery, a3);
+        });
+        qk_done(acc);
+
+        // phase 2: PV(t) on the matrix cores; the masking of tile t+1's
+        // scores (one element per step) on the VALU in between.
+        const uint32_t vsh = visible_bits(t + 1) >> (4 * hsel);
+        // (16 elements over 2*kCB steps: one per step, or 16/(2*kCB))
+        constexpr int kMaskPer = 2 * kCB >= 16 ? 1 : 16 / (2 * kCB);
+        // Scale on the VALU between the MFMAs; the mask after them, and only
+        // for a tile that is not wholly visible (tree keys, the end of the
+        // request, bad slots): a tile of context keys needs none.
+        auto scale_step = [&](int i) {
+#pragma unroll
+          for (int k = 0; k < kMaskPer; ++k) {
+            const int m = i * kMaskPer + k;
+            if (m < 16) {
+              tsc[m] = fmaf(acc[m], L.scale_log2, -mu);
+              asm volatile("" : "+v"(tsc[m]));
+            }
+          }
+        };
+        if constexpr (kAccum) {
+          pv(st, pf, scale_step);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) scale_step(i);
+        }
+        const int p1 = (s + (t + 1) * nsb) * kKeysPerTile;
+        const bool all_visible =
+            p1 + kKeysPerTile <= ctx && __builtin_amdgcn_readfirstlane(bad_s[(t + 1) % kBadRing]) == 0u;
+        if (!all_visible) {
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            tsc[m] = ((vsh >> (8 * (m >> 2) + (m & 3))) & 1u) ? tsc[m] : -INFINITY;
+            asm volatile("" : "+v"(tsc[m]));  // (keeps the branch: no speculative selects)
+          }
+          if constexpr (kMode == kPassAdaptive) overflow |= unset && (vsh & 0x0f0f0f0fu) != 0u;
+        } else {
+          if constexpr (kMode == kPassAdaptive) overflow |= unset;
+        }
       }
+    };
+    int t = 0;
+    for (; t + 3 < ntiles; ++t) step(BoolTag<true>{}, t);
+    for (; t + 1 < ntiles; ++t) step(BoolTag<false>{}, t);
+    // the split's last tile
+    if constexpr (kCompute) {
+      bf16x8 pf[2];
+      softmax(mode_tag, tsc, pf);
+      if constexpr (kAccum) pv(kv_s + ((ntiles - 1) % kStages) * kTileBytes, pf, nothing);
     }
   };
 
-  run_pass(PassMode<kPassAdaptive>{});
   // Workgroup-wide vote: did any row see a score the reference cannot absorb?
   // (the vote is taken by the whole wave: inside `lane == 0` it would see only
   // that lane's row)
-  const bool wave_over = __any(overflow);
-  if (lane == 0) over_s[wid] = wave_over;
-  lds_barrier();
-  bool any_over = false;
+  auto vote = [&]() {
+    const bool wave_over = __any(overflow);
+    if (lane == 0) over_s[wid] = wave_over;
+    lds_barrier();
+    bool any_over = false;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) any_over |= over_s[w] != 0;
-  if (any_over) {  // rare: exact row max first, then accumulate against it
-    run_pass(PassMode<kPassMaxOnly>{});
+    for (int w = 0; w < kWaves; ++w) any_over |= over_s[w] != 0;
+    return any_over;
+  };
+  if (!qk_wave) {
+    lds_barrier();  // (the computing waves' query read-out)
+    run_pass(PassMode<kPassAdaptive>{}, BoolTag<false>{});
+    if (vote()) {
+      run_pass(PassMode<kPassMaxOnly>{}, BoolTag<false>{});
+      run_pass(PassMode<kPassFixed>{}, BoolTag<false>{});
+    }
+    return;
+  }
+  {  // the wave's query rows, from its own stage, into registers
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = ld_k(kv_s + wid * kTileBytes, ks);
+    const int r = rb * (NWQ * 32) + wid * 32 + (fresh(lane) & 31);
+    my_anc = anc_s[(r < L.rows ? r : 0) / fresh(L.heads)];  // this lane's node (divisor rebuilt here too)
+  }
+  lds_barrier();  // the query rows are out of the stages before key tiles land there
+  run_pass(PassMode<kPassAdaptive>{}, BoolTag<true>{});
+  if (vote()) {  // rare: exact row max first, then accumulate against it
+    run_pass(PassMode<kPassMaxOnly>{}, BoolTag<true>{});
     m_ref = m_max;
-    run_pass(PassMode<kPassFixed>{});
+    run_pass(PassMode<kPassFixed>{}, BoolTag<true>{});
   }
 
   // ---- partial result of this split: O / l in fp16 and lse in log2 units,
@@ -1049,11 +1059,12 @@ template <bool kSparse, int NCP>
 void launch_partial_t(const VerifyLaunch& L, hipStream_t stream) {
   const int total = L.batch * L.nsplit * L.row_blocks * NCP;
   const int grid = (total + 7) / 8 * 8;
+  const dim3 block(kWaves * 64);
   switch (L.waves_per_wg) {
-    case 1: hipLaunchKernelGGL((verify_partial_kernel<1, kSparse, NCP>), dim3(grid), dim3(64), 0, stream, L); break;
-    case 2: hipLaunchKernelGGL((verify_partial_kernel<2, kSparse, NCP>), dim3(grid), dim3(128), 0, stream, L); break;
-    case 3: hipLaunchKernelGGL((verify_partial_kernel<3, kSparse, NCP>), dim3(grid), dim3(192), 0, stream, L); break;
-    default: hipLaunchKernelGGL((verify_partial_kernel<4, kSparse, NCP>), dim3(grid), dim3(256), 0, stream, L); break;
+    case 1: hipLaunchKernelGGL((verify_partial_kernel<1, kSparse, NCP>), dim3(grid), block, 0, stream, L); break;
+    case 2: hipLaunchKernelGGL((verify_partial_kernel<2, kSparse, NCP>), dim3(grid), block, 0, stream, L); break;
+    case 3: hipLaunchKernelGGL((verify_partial_kernel<3, kSparse, NCP>), dim3(grid), block, 0, stream, L); break;
+    default: hipLaunchKernelGGL((verify_partial_kernel<4, kSparse, NCP>), dim3(grid), block, 0, stream, L); break;
   }
 }
 

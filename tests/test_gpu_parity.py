@@ -347,3 +347,56 @@ def test_bad_parent_treated_as_root_and_flagged():
     assert err & mv.DEVERR_BAD_PARENT
     tp[0, 4] = -1
     check_parity(case.with_(tree_parent=tp), out, lse, label="bad parent")
+
+
+BF16_NAN, BF16_POS_INF, BF16_NEG_INF = 0x7FC0, 0x7F80, 0xFF80
+
+
+def _referenced_slots(case):
+    used = set()
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        p = np.arange(n)
+        pages = case.page_table[b][p // case.page_size].astype(np.int64)
+        used |= set((pages * case.page_size + p % case.page_size).tolist())
+    return used
+
+
+def test_masked_keys_are_inert_with_non_finite_pool_rows():
+    """Keys that no row may see (an out-of-range page, the padding past each
+    request's last key in its last tile) must enter the products as exact
+    zeros: 0 x NaN would be NaN. Every pool row that no key names, slot 0
+    among them, holds NaN or an infinity; the output must be finite and equal
+    the oracle's on the same request with the masked page removed."""
+    ps = 4
+    case = small_case(seed=504, batch=2, nodes=9, heads=8, contexts=[700, 45], page_size=ps, nsplit=5,
+                      pool_extra=30)
+    pt = case.page_table.copy()
+    num_pages = case.kv.shape[0] // ps
+    if 0 in pt[pt >= 0]:  # make page 0 (slot 0) a page no request names
+        spare = sorted(set(range(num_pages)) - set(pt[pt >= 0].tolist()))[0]
+        kv = case.kv.copy()
+        kv[spare * ps:(spare + 1) * ps] = case.kv[0:ps]
+        pt[pt == 0] = spare
+        case = case.with_(kv=kv, page_table=pt)
+    kv = case.kv.copy()
+    unused = sorted(set(range(kv.shape[0])) - _referenced_slots(case))
+    assert 0 in unused
+    poison = np.array([BF16_NAN, BF16_POS_INF, BF16_NEG_INF], np.uint16)
+    for i, r in enumerate(unused):
+        kv[r] = poison[i % 3]
+    bad_pt = case.page_table.copy()
+    bad_pt[0, 10] = num_pages + 3  # keys 40..43 of request 0: out of range, masked and flagged
+    poisoned = case.with_(kv=kv, page_table=bad_pt)
+    say("masked keys with non-finite unused rows")
+    out, lse, err = run_gpu(poisoned)
+    assert err & mv.DEVERR_SLOT_RANGE
+    o = bf16_bits_to_f64(out)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    # reference: request 0 without its page 10 (keys 40..43), the rest unchanged
+    keep = np.r_[0:10, 11:bad_pt.shape[1]]
+    ref_pt = np.full_like(bad_pt, -1)
+    ref_pt[0, :len(keep)] = case.page_table[0, keep]
+    ref_pt[1] = case.page_table[1]
+    ref_case = case.with_(kv=kv, page_table=ref_pt, seq_lens=case.seq_lens - np.array([4, 0], np.int32))
+    check_parity(ref_case, out, lse, label="inert masked keys")

@@ -110,6 +110,27 @@ def test_sparse_decode_hot_key_exact():
     assert np.all(o[..., 0] == hot % 256 + 1) and np.all(o[..., 1] == hot // 256 + 1) and np.all(o[..., 2:] == 0)
 
 
+def test_sparse_decode_unused_entries_are_inert():
+    """Unused (-1) entries and the padding past each list's length enter the
+    products as exact zeros: with slot 0 and every row no list names set to
+    NaN or an infinity, the output is finite and equals the oracle's."""
+    c = sparse_case(611, batch=3, heads=64, topk=256, pool=4000, lens=[256, 77, 5], holes=0.3, nsplit=8)
+    named = set(c.indices[c.indices >= 0].tolist())
+    if 0 in named:  # keep slot 0 unnamed
+        free = min(set(range(4000)) - named)
+        c.kv[free] = c.kv[0]
+        c.indices[c.indices == 0] = free
+        named = set(c.indices[c.indices >= 0].tolist())
+    poison = np.array([0x7FC0, 0x7F80, 0xFF80], np.uint16)
+    for i, r in enumerate(sorted(set(range(4000)) - named)):
+        c.kv[r] = poison[i % 3]
+    say("sparse decode with non-finite unnamed rows")
+    out, lse, err = run_sparse(c)
+    assert err == 0
+    assert np.all(np.isfinite(bf16_bits_to_f64(out))) and np.all(np.isfinite(lse))
+    check_sparse(c, out, lse, "inert unused entries")
+
+
 def test_sparse_decode_out_of_pool_slot_flagged():
     c = sparse_case(608, batch=1, heads=64, topk=64, pool=1000)
     bad = c.indices.copy()
