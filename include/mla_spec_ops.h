@@ -27,8 +27,8 @@ extern "C" {
 #define MLA_DEVERR_INDEX_RANGE 8u /* an accept length, path entry or length outside its range: clamped */
 
 /* ------------------------------------------------------------------ sparse top-k decode
- * Page "The 24% Ceiling: How Prefill-Decode Disaggregation Saved
- * DeepSeek-V4-Flash on Blackwell", sections "The Decisive Profile" and "The
+ * Page "The 24% Ceiling: When Configuration Tuning Meets the sm_120 Kernel
+ * Wall", sections "The Decisive Profile" and "The
  * Path Forward": a sparse MLA decode attends each head of one query token to
  * the request's 512 selected (top-k) latent rows; the remedy the page names is
  * a split of the selected tokens across the grid. Definition, per request b
@@ -184,7 +184,7 @@ MLA_API mla_status mla_window_map(const int32_t* target_map, int32_t map_stride,
 
 /* ------------------------------------------------------------------ fp8 indexer logits
  * Page "The Indexer Breakthrough: Implementing a Capture-Safe Triton Kernel
- * for DeepSeek-V4's Sparse Attention", sections "The Technical Context" and
+ * for O(actual_seq) Inference", sections "The Technical Context" and
  * "Design Decisions and Assumptions": the DSA indexer scores every cached
  * position of a request: q . k per head, ReLU, times a per-head weight, summed
  * over heads, times the position's scale. The cache is paged in blocks of

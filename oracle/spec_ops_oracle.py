@@ -11,9 +11,8 @@ float64 with exact decoding of the bf16 / e4m3 inputs.
 
 Sources, by function (the readings taken where a page is silent are stated in
 each docstring and collected in the repository's design notes):
-  * sparse_decode: page "The 24% Ceiling: How Prefill-Decode Disaggregation
-    Saved DeepSeek-V4-Flash on Blackwell", section "The Decisive Profile: 63% in
-    One Kernel": a sparse MLA decode attends each head of one query token to a
+  * sparse_decode: page "The 24% Ceiling: When Configuration Tuning Meets the
+    sm_120 Kernel Wall", section "The Decisive Profile: 63% in One Kernel": a sparse MLA decode attends each head of one query token to a
     request's 512 top-k selected tokens; the fix it proposes adds a split over
     the selected tokens to the grid. This is the plain definition: softmax
     attention over the listed latent rows, all heads sharing them (MLA).
@@ -27,7 +26,7 @@ each docstring and collected in the repository's design notes):
   * window_start, compact_len, window_map: page "One Blocking Memcpy Per Verify
     Step", section "The sync, and the bound that replaced it".
   * e4m3_to_f64, indexer_logits: page "The Indexer Breakthrough: Implementing a
-    Capture-Safe Triton Kernel for DeepSeek-V4's Sparse Attention", sections
+    Capture-Safe Triton Kernel for O(actual_seq) Inference", sections
     "The Technical Context" and "Design Decisions and Assumptions".
 """
 
