@@ -128,20 +128,24 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
 // A key row's 1 KiB latent part: 16 bytes per lane from the wave-uniform row
 // address plus the lane offset lane16 ^ x into LDS at lds_base + lds_off +
 // 16*lane. The xor sits between the M0 write and the load, which needs one
-// wait state after it.
+// wait state after it. The row address may come straight from v_readlane (a
+// VALU write of an SGPR), which a VMEM instruction may read only 5 wait states
+// later: the compiler does not see inside this asm, so the block supplies them
+// itself (s_nop 2, the M0 write and the xor).
 __device__ __forceinline__ void dma16_row(const void* row, uint32_t lane16, uint32_t x, uint32_t lds_base,
                                           uint32_t lds_off) {
   uint32_t voff;
-  asm volatile("s_add_u32 m0, %2, %3\n\tv_xor_b32 %0, %4, %5\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 2\n\ts_add_u32 m0, %2, %3\n\tv_xor_b32 %0, %4, %5\n\tglobal_load_lds_dwordx4 %0, %1"
                : "=&v"(voff)
                : "s"(row), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "s"(__builtin_amdgcn_readfirstlane(lds_off)),
                  "s"(__builtin_amdgcn_readfirstlane(x)), "v"(lane16)
                : "memory", "m0", "scc");
 }
 
-// Same, from a wave-uniform base address plus a per-lane 32-bit offset.
+// Same, from a wave-uniform base address plus a per-lane 32-bit offset (5
+// wait states after the asm starts, for a base an earlier VALU wrote).
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 3\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
