@@ -115,13 +115,17 @@ def roof_bound(nodes, heads) -> str:
 
 
 def default_nsplit(batch, nodes, heads, max_keys) -> int:
-    """Enough splits to give every CU a workgroup without chunks below 256 keys."""
+    """NSPLIT for a sweep point: about sqrt(keys) / row blocks, as a power of
+    two, and no more split workgroups than CUs. A split's tiles run one after
+    another (time ~ keys / NSPLIT) while the combine merges NSPLIT partials per
+    row (time ~ NSPLIT x rows); on this GPU the best of {16, ..., 256} at 4k,
+    16k and 64k keys for 9, 16 and 32 nodes follows this rule."""
     rows = nodes * heads
     waves = -(-rows // 32)
     row_blocks = -(-waves // 4)
-    want_wgs = 256
-    per_req = max(1, want_wgs // max(1, batch * row_blocks))
-    return int(max(1, min(per_req, max_keys // 256 if max_keys >= 256 else 1)))
+    cap = max(1, 256 // max(1, batch * row_blocks))
+    root = 1 << max(0, int(math.isqrt(max(1, max_keys))).bit_length() - 1)
+    return int(max(1, min(cap, root // row_blocks)))
 
 
 def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
@@ -370,20 +374,25 @@ def cpu_model():
 
 # ---------------------------------------------------------------- the steps next to verify
 
-def graph_us_per_call(torch, calls, reps=10):
-    """Per-call device time of `calls`, captured in one hipGraph and replayed
-    `reps` times between two events."""
+def graph_us_per_call(torch, calls, reps=4, batches=5):
+    """Per-call device time of `calls`, captured in one hipGraph: the median
+    over `batches` windows of `reps` replays, each between two events (one
+    host stall between two replays, which leaves the GPU idle inside a window,
+    then moves one window rather than the figure)."""
     g = capture(torch, calls)
     g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+    per_call = []
+    for _ in range(batches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) * 1e3 / (reps * len(calls)))
+    return statistics.median(per_call)
 
 
 def _cpu_time(fn, budget_s=5.0, max_reps=5):
