@@ -82,6 +82,10 @@ SMALL = [
     dict(seed=208, batch=1, nodes=3, heads=3, contexts=[5000], page_size=1, tree="uniform", nsplit=64),
     dict(seed=209, batch=1, nodes=8, heads=16, contexts=[70], page_size=2, tree="star", nsplit=100),
     dict(seed=210, batch=2, nodes=20, heads=8, contexts=[4500, 61], page_size=8, tree="uniform", nsplit=2),
+    # the largest tree (64 nodes) with many heads: 1,024 rows in 8 row blocks over two requests, and 4,096 rows
+    # (64 heads, no tensor parallelism) in 32 row blocks
+    dict(seed=212, batch=2, nodes=64, heads=16, contexts=[700, 2049], page_size=1, tree="uniform", nsplit=3),
+    dict(seed=213, batch=1, nodes=64, heads=64, contexts=[300], page_size=8, tree="depth8", nsplit=2),
 ]
 
 
