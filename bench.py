@@ -45,6 +45,8 @@ if ROOT not in sys.path:
 METRIC = "verify-step latency (µs) + effective KV GB/s (% HBM roofline) vs context length"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+# LDS: 256 CUs x 128 B/clk (what 128-bit LDS reads deliver per CU) at 2.4 GHz
+LDS_PEAK_TBS = 256 * 128 * 2.4e9 / 1e12
 QK_DIM, V_DIM = 576, 512
 KV_ROW_BYTES = QK_DIM * 2  # one bf16 latent row per key
 ROTATE_BYTES = 1 << 30     # >= 4 x the 256 MB Infinity Cache
@@ -629,17 +631,41 @@ def parity_of(case, out_bits, lse, ref=None):
                                       np.abs(lse.astype(np.float64) - ref_lse).max() <= 1e-3))
 
 
-def roofline_fields(seq_lens, nodes, heads, page_size, partial_us):
+def partial_lds_bytes(seq_lens, nodes, heads, nsplit) -> int:
+    """LDS bytes the partial kernel's dataflow moves per launch (not a property
+    of the method, of this kernel): for every 32-key tile of a request, every
+    row block and every column part, each computing wave reads the K tile
+    (36,864 B) and the V^T columns of its part (32,768 / parts B), and the
+    tile's 36,864 B arrive in LDS once per workgroup. The column-part rule is
+    the library's: 4 parts while the grid fills at most a quarter of the 256
+    CUs, 2 up to half."""
+    rows = nodes * heads
+    waves = -(-rows // 32)
+    nwq = min(waves, 4)
+    row_blocks = -(-waves // nwq)
+    wgs = len(seq_lens) * nsplit * row_blocks
+    ncp = 4 if wgs * 4 <= 256 else (2 if wgs * 2 <= 256 else 1)
+    tiles = sum(-(-int(n) // 32) for n in seq_lens)
+    tile_bytes = 32 * KV_ROW_BYTES
+    return tiles * row_blocks * ncp * (nwq * (tile_bytes + 32 * V_DIM * 2 // ncp) + tile_bytes)
+
+
+def roofline_fields(seq_lens, nodes, heads, page_size, partial_us, nsplit):
     """The partial kernel against both roofs: algorithmic bytes and flops per
     launch over its measured launch time. `bound` names the roof its
-    arithmetic intensity puts it under."""
+    arithmetic intensity puts it under. Beside them, the LDS bytes of this
+    kernel's dataflow against the LDS peak, the resource its tile loop is
+    actually bound by."""
     pbytes = partial_algorithmic_bytes(seq_lens, nodes, heads, page_size)
     pflops = algorithmic_flops(seq_lens, nodes, heads)
+    lbytes = partial_lds_bytes(seq_lens, nodes, heads, nsplit)
     gbs = pbytes / (partial_us * 1e-6) / 1e9
     tflops = pflops / (partial_us * 1e-6) / 1e12
+    ltbs = lbytes / (partial_us * 1e-6) / 1e12
     return dict(bound=roof_bound(nodes, heads), bytes_per_launch=pbytes, flops_per_launch=pflops,
                 achieved_gbs=gbs, achieved_tflops=tflops, hbm_frac=gbs / HBM_PEAK_GBS,
-                mfma_frac=tflops / BF16_PEAK_TFLOPS)
+                mfma_frac=tflops / BF16_PEAK_TFLOPS, lds_bytes_per_launch=lbytes, lds_tbs=ltbs,
+                lds_frac=ltbs / LDS_PEAK_TBS)
 
 
 def sweep_point(torch, mv, context, nodes, heads=8, nsplit=None, layout="scattered", with_parity=True):
@@ -662,12 +688,13 @@ def sweep_point(torch, mv, context, nodes, heads=8, nsplit=None, layout="scatter
                                                  replicas)
     lat_us = ms * 1e3
     eff = effective_kv_gbs([n], lat_us * 1e-6)
-    rf = roofline_fields([n], nodes, heads, 1, partial_us)
+    rf = roofline_fields([n], nodes, heads, 1, partial_us, nsplit)
     entry = dict(workload=f"context {context}, {nodes}-node tree, {heads} heads, page size 1, {layout} KV rows",
                  layout=layout, context=context, nodes=nodes, rows=nodes * heads, nsplit=nsplit, replicas=replicas,
                  latency_us=round(lat_us, 2), eff_kv_gbs=round(eff, 1), eff_kv_hbm_frac=round(eff / HBM_PEAK_GBS, 4),
                  partial_us=round(partial_us, 2), partial_hbm_frac=round(rf["hbm_frac"], 4),
-                 partial_mfma_frac=round(rf["mfma_frac"], 4), bound=rf["bound"])
+                 partial_mfma_frac=round(rf["mfma_frac"], 4), partial_lds_frac=round(rf["lds_frac"], 4),
+                 bound=rf["bound"])
     if with_parity:
         entry["parity_vs_oracle"] = parity_of(case, out.view(torch.int16).cpu().numpy().view(np.uint16),
                                               lse.cpu().numpy())
@@ -730,7 +757,7 @@ def main():
     lat_us = ms * 1e3
     kvb = kv_bytes(case.seq_lens)
     eff = effective_kv_gbs(case.seq_lens, lat_us * 1e-6)
-    rf = roofline_fields(case.seq_lens, case.num_nodes, case.num_heads, case.page_size, partial_us)
+    rf = roofline_fields(case.seq_lens, case.num_nodes, case.num_heads, case.page_size, partial_us, nsplit)
     traffic = measured_traffic(args.workload)
     if rf["bound"] == "hbm":
         roof = dict(bound="hbm", achieved=round(rf["achieved_gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -742,7 +769,8 @@ def main():
     roof.update(kernel="verify_partial_kernel", kernel_us=round(partial_us, 3), bytes_per_launch=rf["bytes_per_launch"],
                 flops_per_launch=rf["flops_per_launch"], hbm_gbs=round(rf["achieved_gbs"], 1),
                 hbm_frac=round(rf["hbm_frac"], 4), mfma_tflops=round(rf["achieved_tflops"], 1),
-                mfma_frac=round(rf["mfma_frac"], 4))
+                mfma_frac=round(rf["mfma_frac"], 4), lds_bytes_per_launch=rf["lds_bytes_per_launch"],
+                lds_tbs=round(rf["lds_tbs"], 2), lds_peak_tbs=round(LDS_PEAK_TBS, 1), lds_frac=round(rf["lds_frac"], 4))
     if traffic:
         roof["traffic_over_algorithmic"] = round(traffic / rf["bytes_per_launch"], 3)
     gpu_out = out.view(torch.int16).cpu().numpy().view(np.uint16)
