@@ -263,7 +263,9 @@ def time_rotating(torch, make_call, replicas, steps, warmup):
     """Device time of exactly `steps` calls that cycle over the replicas
     (call i reads replica i mod R), as ms per call.
 
-    Every graph is captured first (capture runs each call once, eagerly). The
+    Every graph is captured first (capture runs each call once, eagerly) and
+    replayed once before the timed window, so that no graph is launched for
+    the first time inside it (a first launch also uploads the graph). The
     warmup then replays whole cycles (at least `warmup` calls, ending on
     replica R-1), and the timed calls start at replica 0. So every timed call,
     however few there are, reads a replica last touched R-1 calls earlier: R-1
@@ -273,6 +275,8 @@ def time_rotating(torch, make_call, replicas, steps, warmup):
     g_cycle = capture(torch, [make_call(i % replicas) for i in range(per)])
     rem = steps % per
     g_rem = capture(torch, [make_call(i % replicas) for i in range(rem)]) if rem else None
+    if g_rem is not None:
+        g_rem.replay()
     warm_cycles = max(1, -(-warmup // per))
     for _ in range(warm_cycles):
         g_cycle.replay()
@@ -286,7 +290,7 @@ def time_rotating(torch, make_call, replicas, steps, warmup):
         g_rem.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, warm_cycles * per
+    return e0.elapsed_time(e1) / steps, warm_cycles * per + rem
 
 
 def time_workload(torch, mv, rep: Replicated, nodes, heads, nsplit, sm_scale, steps, warmup):
